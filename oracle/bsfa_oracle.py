@@ -1,0 +1,293 @@
+"""CPU float64 oracle for block-sparse FlashAttention prefill (BSFA form).
+
+TEST INFRASTRUCTURE.  Only the test suite, the package smoke check and the
+benchmark's CPU-baseline leg may import this module.  It is the definition
+the HIP path is checked against and it shares no code with that path: it
+imports nothing from the kernel package and the kernel package imports
+nothing from here.
+
+Source: "Block Sparse Flash Attention" (paperpeel.com/paper/2512.07011).
+
+What is computed, per batch b and query head h (KV head g = h // G):
+
+* Scores are the scaled dot products S = Q K^T / sqrt(d)            (Sec. 2,
+  "Scaled dot-product attention"; App. B.2 step (3)).
+* Queries are cut into blocks of ``block`` rows, keys into blocks of
+  ``block`` columns; tile (i, j) pairs query block i with key block j
+  (App. B.2).  Under causal masking key k is visible to query q iff k <= q,
+  and tiles with j > i hold no visible pair, so they are not computed
+  (App. B.2, "approximately half for causal").
+* Each computed tile has a maximum score s_max(i, j), taken over its visible
+  entries (Sec. 4.1).
+* The threshold for head h and query block i is T[h, min(i, T_len - 1)]:
+  per (head, position) (Sec. 4.1, 4.2), with positions past the table
+  reusing its last entry (App. B.3, "Practical considerations").
+* Tile (i, j) is skipped iff it is off the diagonal and s_max(i, j) < T
+  (strict, Sec. 4.4); diagonal tiles always pass (Sec. 4.1).  A NaN threshold
+  compares false, so nothing is skipped.
+* A skipped tile takes no part in the running max, sum or output (Sec. 4.4).
+  Online softmax over the kept tiles is an exact rearrangement of one softmax
+  over the kept entries (App. B.2), so the oracle evaluates that softmax
+  directly: lse[q] = log sum_{k in R(q)} exp S[q, k] and
+  O[q] = sum_{k in R(q)} exp(S[q, k] - lse[q]) V[k], where R(q) is the set
+  of visible keys in kept tiles.  R(q) always holds k = q (diagonal tile).
+
+Readings where the pages are silent (each is listed in the design notes):
+the gate uses the scaled score; the tile max runs over visible entries only;
+GQA groups are contiguous (g = h // (H_q / H_kv)); lse is the natural log of
+the scaled scores over R(q); ties (s_max == T) are kept.
+
+Threshold calibration (Sec. 4.2, App. B.3): for each query block, sort the
+off-diagonal computed tiles by their maxima and put the threshold so exactly
+the top k are retained - here the midpoint between the k-th and (k+1)-th
+largest maxima, or -inf when the block has at most k off-diagonal tiles -
+then average over calibration samples (the batch axis).
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "to_f64",
+    "block_scores",
+    "block_tile_maxima",
+    "threshold_for",
+    "gate",
+    "masked_softmax_attention",
+    "run_blocks",
+    "run",
+    "tile_maxima",
+    "calibrate_fixed_k",
+    "STATE_PRUNED",
+    "STATE_KEPT",
+    "STATE_SKIPPED",
+    "STATE_DIAGONAL",
+]
+
+# tile_state codes
+STATE_PRUNED = 0  # causal: tile above the diagonal, never computed
+STATE_KEPT = 1  # off-diagonal tile that passed the gate
+STATE_SKIPPED = 2  # off-diagonal tile below its threshold
+STATE_DIAGONAL = 3  # diagonal tile (bypasses the gate)
+
+
+def to_f64(x: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> float64, exactly; float arrays pass through."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def block_scores(q_rows: np.ndarray, k_cols: np.ndarray, head_dim: int) -> np.ndarray:
+    """Scaled scores S = Q_i K^T / sqrt(d) of one query block (Sec. 2; App. B.2 step (3))."""
+    return (q_rows @ k_cols.T) / math.sqrt(head_dim)
+
+
+def _visible(i: int, block: int, n_keys: int, causal: bool) -> np.ndarray:
+    """Visibility of keys [0, n_keys) to the rows of query block i."""
+    qpos = np.arange(i * block, (i + 1) * block)[:, None]
+    kpos = np.arange(n_keys)[None, :]
+    if causal:
+        return kpos <= qpos
+    return np.ones((block, n_keys), dtype=bool)
+
+
+def block_tile_maxima(s: np.ndarray, vis: np.ndarray, block: int) -> np.ndarray:
+    """s_max(i, j) over the visible entries of each computed key block j (Sec. 4.1)."""
+    n_tiles = s.shape[1] // block
+    out = np.empty(n_tiles)
+    for j in range(n_tiles):
+        cols = slice(j * block, (j + 1) * block)
+        out[j] = s[:, cols][vis[:, cols]].max()
+    return out
+
+
+def threshold_for(thresholds: np.ndarray, h: int, i: int) -> float:
+    """T[h, i] with positions past the table reusing the last entry (App. B.3)."""
+    t_len = thresholds.shape[1]
+    return float(thresholds[h, min(i, t_len - 1)])
+
+
+def gate(tile_max_row: np.ndarray, i: int, tau: float) -> np.ndarray:
+    """Skip decision of the computed tiles of query block i (Sec. 4.1, 4.4).
+
+    Skip iff off-diagonal and s_max < tau (strict).  ``tau`` NaN compares false.
+    """
+    skip = tile_max_row < tau
+    if i < skip.shape[0]:
+        skip[i] = False  # diagonal bypass
+    return skip
+
+
+def masked_softmax_attention(s: np.ndarray, keep: np.ndarray, v_rows: np.ndarray):
+    """lse and output of softmax restricted to ``keep`` (App. B.2 + Sec. 4.4).
+
+    lse[q] = log sum_{k: keep} exp s[q, k];  O[q] = sum_{k: keep} exp(s[q,k] - lse[q]) V[k].
+    Every row must keep at least one entry.
+    """
+    if not keep.any(axis=1).all():
+        raise ValueError("a query row keeps no key")
+    # only keys some row keeps enter the arithmetic: a skipped tile's V rows
+    # are never read (Sec. 4.4)
+    cols = np.flatnonzero(keep.any(axis=0))
+    s_kept = np.where(keep[:, cols], s[:, cols], -np.inf)
+    m = s_kept.max(axis=1, keepdims=True)
+    lse = m[:, 0] + np.log(np.exp(s_kept - m).sum(axis=1))
+    p = np.exp(s_kept - lse[:, None])  # exp(-inf) = 0 outside keep
+    return p @ v_rows[cols], lse
+
+
+def run_blocks(
+    q: np.ndarray,
+    k: np.ndarray,
+    v: np.ndarray,
+    thresholds: np.ndarray,
+    causal: bool,
+    block: int,
+    blocks: Iterable[Tuple[int, int, int]],
+    skip_override: Optional[np.ndarray] = None,
+) -> List[dict]:
+    """Evaluate selected query blocks ``(b, h, i)``.
+
+    q: [B, H_q, N, d], k/v: [B, H_kv, N, d] (bf16 bits or floats);
+    thresholds: [H_q, T_len].  ``skip_override`` ([B, H_q, M, M] bool) replaces
+    the gate's decisions when given (diagonal tiles must stay kept).
+
+    Each result holds ``out`` [block, d], ``lse`` [block], ``tile_max`` [M]
+    (NaN where not computed), ``tile_state`` [M] uint8 and ``skip_count``.
+    """
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if Hq % Hkv:
+        raise ValueError("H_q must be a multiple of H_kv")
+    G = Hq // Hkv
+    M = N // block
+    results = []
+    cache = {}
+    for b, h, i in blocks:
+        g = h // G
+        key = (b, g)
+        if key not in cache:
+            cache.clear()
+            cache[key] = (to_f64(k[b, g]), to_f64(v[b, g]))
+        kf, vf = cache[key]
+        n_keys = (i + 1) * block if causal else N
+        q_rows = to_f64(q[b, h, i * block : (i + 1) * block])
+        s = block_scores(q_rows, kf[:n_keys], d)
+        vis = _visible(i, block, n_keys, causal)
+        tmax = block_tile_maxima(s, vis, block)
+        tau = threshold_for(thresholds, h, i)
+        if skip_override is not None:
+            skip = np.array(skip_override[b, h, i, : tmax.shape[0]], dtype=bool)
+            if skip[i]:
+                raise ValueError("a diagonal tile cannot be skipped")
+        else:
+            skip = gate(tmax, i, tau)
+        keep = vis & ~np.repeat(skip, block)[None, :]
+        out, lse = masked_softmax_attention(s, keep, vf[:n_keys])
+        tile_max = np.full(M, np.nan)
+        tile_max[: tmax.shape[0]] = tmax
+        state = np.full(M, STATE_PRUNED, dtype=np.uint8)
+        state[: tmax.shape[0]] = np.where(skip, STATE_SKIPPED, STATE_KEPT)
+        state[i] = STATE_DIAGONAL
+        results.append(
+            {
+                "b": b,
+                "h": h,
+                "i": i,
+                "out": out,
+                "lse": lse,
+                "tile_max": tile_max,
+                "tile_state": state,
+                "skip_count": int(skip.sum()),
+                "tau": tau,
+            }
+        )
+    return results
+
+
+def run(q, k, v, thresholds, causal: bool, block: int, skip_override=None) -> dict:
+    """Whole-layer oracle: out [B,H_q,N,d], lse [B,H_q,N], skip_counts [B,H_q,M],
+    tile_state [B,H_q,M,M] (uint8), tile_max [B,H_q,M,M] (NaN where not computed)."""
+    B, Hq, N, d = q.shape
+    M = N // block
+    out = np.empty((B, Hq, N, d))
+    lse = np.empty((B, Hq, N))
+    skip_counts = np.empty((B, Hq, M), dtype=np.int64)
+    tile_state = np.empty((B, Hq, M, M), dtype=np.uint8)
+    tile_max = np.empty((B, Hq, M, M))
+    blocks = [(b, h, i) for b in range(B) for h in range(Hq) for i in range(M)]
+    for r in run_blocks(q, k, v, thresholds, causal, block, blocks, skip_override):
+        b, h, i = r["b"], r["h"], r["i"]
+        rows = slice(i * block, (i + 1) * block)
+        out[b, h, rows] = r["out"]
+        lse[b, h, rows] = r["lse"]
+        skip_counts[b, h, i] = r["skip_count"]
+        tile_state[b, h, i] = r["tile_state"]
+        tile_max[b, h, i] = r["tile_max"]
+    return {
+        "out": out,
+        "lse": lse,
+        "skip_counts": skip_counts,
+        "tile_state": tile_state,
+        "tile_max": tile_max,
+    }
+
+
+def tile_maxima(q, k, causal: bool, block: int, heads: Optional[Sequence[int]] = None,
+                rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """s_max of every computed tile: [B, H_q, M, M] float64, NaN where not computed.
+
+    ``heads`` / ``rows`` restrict the evaluation (other entries stay NaN).
+    """
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    M = N // block
+    out = np.full((B, Hq, M, M), np.nan)
+    heads = range(Hq) if heads is None else heads
+    rows = range(M) if rows is None else rows
+    for b in range(B):
+        for h in heads:
+            kf = to_f64(k[b, h // G])
+            for i in rows:
+                n_keys = (i + 1) * block if causal else N
+                s = block_scores(to_f64(q[b, h, i * block : (i + 1) * block]), kf[:n_keys], d)
+                tm = block_tile_maxima(s, _visible(i, block, n_keys, causal), block)
+                out[b, h, i, : tm.shape[0]] = tm
+    return out
+
+
+def calibrate_fixed_k(tile_max: np.ndarray, k: int, causal: bool) -> np.ndarray:
+    """Fixed-k thresholds [H_q, M] from sample tile maxima [S, H_q, M, M] (Sec. 4.2, App. B.3).
+
+    Per sample, head and query block i: the off-diagonal computed tiles are
+    sorted by their maxima (largest first).  With n_i of them, the threshold
+    is -inf if n_i <= k, else the midpoint of the k-th and (k+1)-th largest
+    (+inf for k = 0), so that (barring ties) exactly the top k are retained.
+    The thresholds of the samples are then averaged.
+    """
+    if k < 0:
+        raise ValueError("k must be >= 0")
+    S, Hq, M, _ = tile_max.shape
+    thr = np.zeros((Hq, M))
+    for h in range(Hq):
+        for i in range(M):
+            cols = [j for j in (range(i) if causal else range(M)) if j != i]
+            if len(cols) <= k:
+                thr[h, i] = -np.inf
+                continue
+            acc = 0.0
+            for s_idx in range(S):
+                vals = np.sort(tile_max[s_idx, h, i, cols])[::-1]
+                if np.isnan(vals).any():
+                    raise ValueError("tile maxima missing for a calibrated row")
+                # k = 0 retains no off-diagonal tile: a threshold above every maximum
+                acc += 0.5 * (vals[k - 1] + vals[k]) if k > 0 else np.inf
+            thr[h, i] = acc / S
+    return thr

@@ -1,0 +1,71 @@
+"""Plant plausible mistakes in the oracle (CPU) and check that a pin catches each.
+
+Each mutant replaces one function of the oracle module for the duration of a
+test; the pin that guards the corresponding passage must then fail.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import bsfa_oracle as ob
+import test_oracle_pins as pins
+
+
+def _mut_gate_le(tile_max_row, i, tau):  # '<=' instead of the strict '<'
+    skip = tile_max_row <= tau
+    skip[i] = False
+    return skip
+
+
+def _mut_gate_no_bypass(tile_max_row, i, tau):  # diagonal gated like the rest
+    return tile_max_row < tau
+
+
+def _mut_unscaled(q_rows, k_cols, head_dim):  # scores without 1/sqrt(d)
+    return q_rows @ k_cols.T
+
+
+def _mut_threshold_wrap(thresholds, h, i):  # wraps positions instead of reusing the last
+    return float(thresholds[h, i % thresholds.shape[1]])
+
+
+def _mut_tile_max_all(s, vis, block):  # maximum over masked entries too
+    n = s.shape[1] // block
+    return np.array([s[:, j * block:(j + 1) * block].max() for j in range(n)])
+
+
+_ORIG_RUN_BLOCKS = ob.run_blocks
+
+
+def _mut_gqa_modulo(q, k, v, thresholds, causal, block, blocks, skip_override=None):
+    # KV head h % H_kv instead of the contiguous h // G: permute q heads so the
+    # real routine sees the interleaved grouping
+    Hq, Hkv = q.shape[1], k.shape[1]
+    G = Hq // Hkv
+    perm = np.array([(h % Hkv) * G + h // Hkv for h in range(Hq)])
+    res = _ORIG_RUN_BLOCKS(q[:, perm], k, v, thresholds[perm], causal, block,
+                           [(b, int(np.flatnonzero(perm == h)[0]), i) for b, h, i in blocks], skip_override)
+    for r, (b, h, i) in zip(res, blocks):
+        r["h"] = h
+    return res
+
+
+MUTANTS = [
+    ("gate", _mut_gate_le, lambda: pins.test_uniform_scores_tie_rule_closed_form(True)),
+    ("gate", _mut_gate_no_bypass, lambda: pins.test_infinite_threshold_is_block_diagonal_attention(True)),
+    ("block_scores", _mut_unscaled, lambda: pins.test_dense_threshold_equals_library_attention(True)),
+    ("threshold_for", _mut_threshold_wrap, pins.test_threshold_table_reuses_last_entry),
+    ("block_tile_maxima", _mut_tile_max_all,
+     lambda: pins.test_oracle_matches_brute_force_streaming(True, 1, 2, 1, 256, 16, 4, 3)),
+    ("run_blocks", _mut_gqa_modulo, lambda: pins.test_dense_threshold_equals_library_attention(False)),
+]
+
+
+@pytest.mark.parametrize("name,mutant,pin", MUTANTS, ids=[m[1].__name__ for m in MUTANTS])
+def test_pin_catches_mutant(monkeypatch, name, mutant, pin):
+    monkeypatch.setattr(ob, name, mutant)
+    with pytest.raises((AssertionError, ValueError)):
+        pin()
