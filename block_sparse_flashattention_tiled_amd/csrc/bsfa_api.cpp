@@ -1,0 +1,133 @@
+// C ABI of the block-sparse FlashAttention prefill library (declared in
+// include/bsfa.h).  Host code only: argument checks, parameter packing and
+// dispatch to the HIP kernels.  Nothing here allocates device memory.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "bsfa.h"
+#include "bsfa_internal.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_shape(const bsfa_shape& s, int causal, const bsfa_block& blk) {
+  if (s.batch < 1 || s.n_heads_q < 1 || s.n_heads_kv < 1 || s.seq_len < 1 || s.head_dim < 1 || s.thr_len < 1)
+    return BSFA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return BSFA_ERR_SHAPE;
+  if (s.n_heads_q % s.n_heads_kv) return BSFA_ERR_SHAPE;
+  if (blk.bm < 1 || blk.bn < 1) return BSFA_ERR_SHAPE;
+  if (blk.bm != blk.bn) return BSFA_ERR_UNSUPPORTED;
+  if (blk.bm != 64 && blk.bm != 128) return BSFA_ERR_UNSUPPORTED;
+  if (s.head_dim != 64 && s.head_dim != 128) return BSFA_ERR_UNSUPPORTED;
+  if (s.seq_len % blk.bm) return BSFA_ERR_SHAPE;
+  // the kernels index heads, rows and thresholds with 32-bit integers
+  const int64_t lim = INT32_MAX;
+  const int64_t m = s.seq_len / blk.bm;
+  if (s.seq_len > lim / 2 || s.batch > lim || s.n_heads_q > lim) return BSFA_ERR_SHAPE;
+  if (s.batch * s.n_heads_q > lim / m) return BSFA_ERR_SHAPE;    // workgroups
+  if (s.n_heads_q > lim / s.thr_len) return BSFA_ERR_SHAPE;      // threshold index
+  if (s.batch * s.n_heads_q > lim / s.seq_len) return BSFA_ERR_SHAPE;  // (b, h) row base
+  return BSFA_OK;
+}
+
+bsfa::FwdParams shape_params(const bsfa_shape& shape, const bsfa_block& block) {
+  bsfa::FwdParams p{};
+  p.B = (int)shape.batch;
+  p.Hq = (int)shape.n_heads_q;
+  p.Hkv = (int)shape.n_heads_kv;
+  p.G = p.Hq / p.Hkv;
+  p.N = (int)shape.seq_len;
+  p.M = (int)(shape.seq_len / block.bm);
+  p.T_len = (int)shape.thr_len;
+  p.scale = (float)(1.0 / sqrt((double)shape.head_dim));
+  p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)shape.head_dim));
+  const int64_t grid = (int64_t)p.B * p.Hq * p.M;
+  p.remap = (grid % (8 * (int64_t)p.G) == 0) ? 1 : 0;
+  return p;
+}
+
+int prefill_impl(const void* q, const void* k, const void* v, float* out, float* lse, int32_t* skip_counts,
+                 const float* thresholds, bsfa_shape shape, int causal, bsfa_block block, uint8_t* tile_state,
+                 float* tile_max, int diagnostics, void* stream) {
+  const int st = check_shape(shape, causal, block);
+  if (st != BSFA_OK) return st;
+  if (!q || !k || !v || !out || !thresholds) return BSFA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return BSFA_ERR_ALIGN;
+  if (!aligned(thresholds, 4) || (lse && !aligned(lse, 4)) || (skip_counts && !aligned(skip_counts, 4)) ||
+      (tile_max && !aligned(tile_max, 4)))
+    return BSFA_ERR_ALIGN;
+
+  bsfa::FwdParams p = shape_params(shape, block);
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.out = out;
+  p.lse = lse;
+  p.skip_counts = skip_counts;
+  p.thresholds = thresholds;
+  p.tile_state = tile_state;
+  p.tile_max = tile_max;
+  return bsfa::launch_fwd(p, (int)shape.head_dim, block.bm, causal, diagnostics,
+                          static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int bsfa_validate(bsfa_shape shape, int causal, bsfa_block block) { return check_shape(shape, causal, block); }
+
+const char* bsfa_status_string(int status) {
+  switch (status) {
+    case BSFA_OK: return "ok";
+    case BSFA_ERR_NULL: return "a required pointer is NULL";
+    case BSFA_ERR_SHAPE: return "inconsistent or out-of-range shape";
+    case BSFA_ERR_UNSUPPORTED: return "unsupported head_dim / tile combination";
+    case BSFA_ERR_ALIGN: return "misaligned pointer";
+    case BSFA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int bsfa_prefill(const void* q, const void* k, const void* v, float* out, float* lse, int32_t* skip_counts,
+                 const float* thresholds, bsfa_shape shape, int causal, bsfa_block block, void* stream) {
+  return prefill_impl(q, k, v, out, lse, skip_counts, thresholds, shape, causal, block, nullptr, nullptr, 0,
+                      stream);
+}
+
+int bsfa_prefill_ex(const void* q, const void* k, const void* v, float* out, float* lse, int32_t* skip_counts,
+                    const float* thresholds, bsfa_shape shape, int causal, bsfa_block block, uint8_t* tile_state,
+                    float* tile_max, void* stream) {
+  return prefill_impl(q, k, v, out, lse, skip_counts, thresholds, shape, causal, block, tile_state, tile_max, 1,
+                      stream);
+}
+
+int bsfa_tile_max(const void* q, const void* k, float* tile_max, bsfa_shape shape, int causal, bsfa_block block,
+                  void* stream) {
+  const int st = check_shape(shape, causal, block);
+  if (st != BSFA_OK) return st;
+  if (!q || !k || !tile_max) return BSFA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(tile_max, 4)) return BSFA_ERR_ALIGN;
+  bsfa::FwdParams p = shape_params(shape, block);
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.tile_max = tile_max;
+  return bsfa::launch_fwd(p, (int)shape.head_dim, block.bm, causal, 2, static_cast<hipStream_t>(stream));
+}
+
+int bsfa_calibrate_fixed_k(const float* tile_max, int64_t n_samples, int64_t n_heads, int64_t n_blocks, int causal,
+                           int64_t k, float* thresholds, void* stream) {
+  if (n_samples < 1 || n_heads < 1 || n_blocks < 1 || k < 0 || (causal != 0 && causal != 1))
+    return BSFA_ERR_SHAPE;
+  if (n_blocks > bsfa::kCalibMaxBlocks) return BSFA_ERR_UNSUPPORTED;
+  if (n_heads * n_blocks > INT32_MAX || n_samples > INT32_MAX) return BSFA_ERR_SHAPE;
+  if (!tile_max || !thresholds) return BSFA_ERR_NULL;
+  if (!aligned(tile_max, 4) || !aligned(thresholds, 4)) return BSFA_ERR_ALIGN;
+  const int kk = (int)(k < n_blocks ? k : n_blocks);
+  return bsfa::launch_calibrate(tile_max, (int)n_samples, (int)n_heads, (int)n_blocks, causal, kk, thresholds,
+                                static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

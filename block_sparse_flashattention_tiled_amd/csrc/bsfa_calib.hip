@@ -1,0 +1,74 @@
+// Fixed-k threshold calibration on the GPU.
+//
+// "Block Sparse Flash Attention" (paperpeel.com/paper/2512.07011), Sec. 4.2
+// and App. B.3: for each query block, the off-diagonal blocks are ordered by
+// their maximum scores and the threshold is placed so that exactly the top k
+// are retained; thresholds are averaged over calibration samples.
+//
+// Input: the tile maxima of every computed tile, [S, H, M, M] (S samples,
+// e.g. the batch axis of a tile-max pass).  Output: thresholds [H, M].
+// For query block i with n_i off-diagonal computed tiles (causal: i,
+// bidirectional: M - 1): -inf if n_i <= k; +inf if k == 0; otherwise the
+// midpoint of the k-th and (k+1)-th largest maxima, averaged over samples.
+//
+// One workgroup per (head, query block).  The order statistics are found by
+// rank counting in LDS (rank = number of larger values, ties broken by
+// position), which is exact and deterministic; O(n_i^2) comparisons per row.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "bsfa_internal.h"
+
+namespace bsfa {
+
+constexpr int CALIB_THREADS = 256;
+
+__global__ void __launch_bounds__(CALIB_THREADS)
+    bsfa_calib_kernel(const float* __restrict__ tile_max, int S, int H, int M, int causal, int k,
+                      float* __restrict__ thr) {
+  extern __shared__ float vals[];
+  __shared__ float sel[2];
+  const int h = blockIdx.x / M;
+  const int i = blockIdx.x % M;
+  const int tid = threadIdx.x;
+  const int n = causal ? i : M - 1;
+  if (n <= k) {
+    if (tid == 0) thr[(size_t)h * M + i] = -INFINITY;
+    return;
+  }
+  if (k == 0) {
+    if (tid == 0) thr[(size_t)h * M + i] = INFINITY;
+    return;
+  }
+  float acc = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float* row = tile_max + (((size_t)s * H + h) * M + i) * M;
+    for (int t = tid; t < n; t += CALIB_THREADS) vals[t] = row[t < i ? t : t + 1];
+    __syncthreads();
+    for (int t = tid; t < n; t += CALIB_THREADS) {
+      const float x = vals[t];
+      int rank = 0;
+      for (int u = 0; u < n; ++u) {
+        const float y = vals[u];
+        rank += (y > x || (y == x && u < t)) ? 1 : 0;
+      }
+      if (rank == k - 1) sel[0] = x;
+      if (rank == k) sel[1] = x;
+    }
+    __syncthreads();
+    acc += 0.5f * (sel[0] + sel[1]);
+    __syncthreads();
+  }
+  if (tid == 0) thr[(size_t)h * M + i] = acc / (float)S;
+}
+
+int launch_calibrate(const float* tile_max, int S, int H, int M, int causal, int k, float* thr,
+                     hipStream_t stream) {
+  const size_t lds = (size_t)M * sizeof(float);
+  hipLaunchKernelGGL(bsfa_calib_kernel, dim3((unsigned)((size_t)H * M)), dim3(CALIB_THREADS), lds, stream,
+                     tile_max, S, H, M, causal, k, thr);
+  return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+}  // namespace bsfa

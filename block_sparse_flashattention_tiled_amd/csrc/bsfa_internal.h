@@ -1,0 +1,38 @@
+// Internal interface between the C ABI (bsfa_api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsfa {
+
+// Arguments of one forward launch; pointers are device pointers.
+struct FwdParams {
+  const uint16_t* q;  // bf16 [B, Hq, N, d]
+  const uint16_t* k;  // bf16 [B, Hkv, N, d]
+  const uint16_t* v;  // bf16 [B, Hkv, N, d]
+  float* out;         // fp32 [B, Hq, N, d]
+  float* lse;         // fp32 [B, Hq, N] or null
+  int32_t* skip_counts;     // int32 [B, Hq, M] or null
+  const float* thresholds;  // fp32 [Hq, T_len]
+  uint8_t* tile_state;      // uint8 [B, Hq, M, M] or null (diagnostic launches only)
+  float* tile_max;          // fp32 [B, Hq, M, M] or null (diagnostic launches only)
+  int B, Hq, Hkv, G, N, M, T_len;
+  float scale;       // 1 / sqrt(d)
+  float scale_log2;  // scale * log2(e)
+  int remap;         // 1: XCD-aware workgroup order applies (grid % (8 * G) == 0)
+};
+
+// Enqueue the forward kernel; mode 0 = forward, 1 = forward with per-tile
+// diagnostics, 2 = tile maxima only.  Returns a BSFA_* status.
+int launch_fwd(const FwdParams& p, int head_dim, int block, int causal, int mode, hipStream_t stream);
+
+// Enqueue the fixed-k calibration over tile maxima [S, H, M, M] -> thresholds [H, M].
+int launch_calibrate(const float* tile_max, int S, int H, int M, int causal, int k, float* thr,
+                     hipStream_t stream);
+
+// Largest number of query blocks the calibration kernel handles (one row of
+// tile maxima must fit in LDS).
+constexpr int kCalibMaxBlocks = 16384;
+
+}  // namespace bsfa

@@ -1,0 +1,162 @@
+/*
+ * bsfa.h - C ABI of the block-sparse FlashAttention prefill library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one defined in "Block Sparse Flash Attention"
+ * (paperpeel.com/paper/2512.07011): FlashAttention-2 style tiled attention
+ * (Sec. 2 "FlashAttention", App. B.2) in which every score tile is computed
+ * exactly and its maximum scaled score is compared with a calibrated
+ * threshold for its head and query block (Sec. 4, 4.1).  A tile below the
+ * threshold is skipped: its V block is not loaded, the P.V product is not
+ * performed and the running max / sum / output are not updated (Sec. 4.4).
+ * Diagonal tiles always pass (Sec. 4.1).  Under causal masking, tiles above
+ * the diagonal are not computed at all (App. B.2).
+ *
+ * Conventions shared by every entry point:
+ *  - Tensor pointers are DEVICE pointers owned by the caller (for instance
+ *    torch tensors).  The library allocates no device memory, keeps no
+ *    reference after a call returns and holds no global state; calls are
+ *    reentrant.
+ *  - Every argument check runs on the host before anything is enqueued; on
+ *    error the call returns a non-zero status and writes nothing.
+ *  - Work is enqueued on ``stream`` (a hipStream_t; NULL = the default
+ *    stream).  No call synchronises.  A launch failure reported by the HIP
+ *    runtime is returned as BSFA_ERR_LAUNCH; faults during execution surface
+ *    at the caller's next synchronisation, as for any HIP work.
+ *  - No C++ exception crosses this interface.
+ *  - Results are deterministic: no atomics, fixed reduction order.
+ */
+#ifndef BSFA_H
+#define BSFA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Problem shape.  Query head h reads KV head h / (n_heads_q / n_heads_kv)
+ * (contiguous groups; the pages do not fix the grouped-query mapping). */
+typedef struct {
+  int64_t batch;      /* B    >= 1 */
+  int64_t n_heads_q;  /* H_q  >= 1 */
+  int64_t n_heads_kv; /* H_kv >= 1, H_q % H_kv == 0 */
+  int64_t seq_len;    /* N    >= 1 and a multiple of the block size.  The pages
+                         pad a non-aligned sequence by repeating its last token
+                         (App. B.3); that padding is the caller's. */
+  int64_t head_dim;   /* d in {64, 128} */
+  int64_t thr_len;    /* T_len >= 1: thresholds per head.  Query block i uses
+                         entry min(i, T_len - 1): blocks past the table reuse
+                         its last entry (App. B.3). */
+} bsfa_shape;
+
+/* Tile shape B_M x B_N (App. B.2).  This build supports square tiles with
+ * bm == bn in {64, 128}; the tile is also the skip granularity. */
+typedef struct {
+  int32_t bm;
+  int32_t bn;
+} bsfa_block;
+
+enum {
+  BSFA_OK = 0,
+  BSFA_ERR_NULL = 1,        /* a required pointer is NULL */
+  BSFA_ERR_SHAPE = 2,       /* inconsistent or out-of-range shape */
+  BSFA_ERR_UNSUPPORTED = 3, /* valid shape this build has no kernel for */
+  BSFA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  BSFA_ERR_LAUNCH = 5       /* the HIP runtime refused the launch */
+};
+
+/* Tile states written by bsfa_prefill_ex. */
+enum {
+  BSFA_TILE_PRUNED = 0,   /* causal: above the diagonal, never computed */
+  BSFA_TILE_KEPT = 1,     /* off-diagonal, s_max >= threshold (or threshold NaN) */
+  BSFA_TILE_SKIPPED = 2,  /* off-diagonal, s_max < threshold: no V load, no P.V */
+  BSFA_TILE_DIAGONAL = 3  /* diagonal tile: bypasses the gate */
+};
+
+/*
+ * bsfa_prefill - block-sparse attention forward (prefill) for one layer.
+ *
+ *  q           bf16  [B, H_q,  N, d] contiguous, read only
+ *  k           bf16  [B, H_kv, N, d] contiguous, read only
+ *  v           bf16  [B, H_kv, N, d] contiguous, read only; rows of V in tiles
+ *                    that every query block skips are never read
+ *  out         fp32  [B, H_q,  N, d] fully overwritten:
+ *                    O[q] = sum_{k in R(q)} softmax(S)[q,k] V[k] with
+ *                    S = Q K^T / sqrt(d) (Sec. 2) and R(q) the visible keys
+ *                    of the kept tiles of q's query block
+ *  lse         fp32  [B, H_q, N] natural-log sum of exp(S) over R(q); NULL = not written
+ *  skip_counts int32 [B, H_q, N / bm] number of skipped tiles per query block;
+ *                    NULL = not written
+ *  thresholds  fp32  [H_q, T_len] in the scaled-score domain (the same units
+ *                    as S).  Tile (i, j), j != i, is skipped iff
+ *                    max_{visible (q,k) in tile} S[q,k] < thresholds[h, min(i, T_len-1)]
+ *                    (strict, Sec. 4.4).  -inf keeps every tile (dense
+ *                    attention); +inf keeps only the diagonal; NaN keeps all.
+ *  shape, causal (0 or 1), block: see above.
+ *  stream      hipStream_t or NULL.
+ *
+ * Returns BSFA_OK or an error status (see the enum); nothing is written on error.
+ */
+int bsfa_prefill(const void* q, const void* k, const void* v, float* out, float* lse, int32_t* skip_counts,
+                 const float* thresholds, bsfa_shape shape, int causal, bsfa_block block, void* stream);
+
+/*
+ * bsfa_prefill_ex - bsfa_prefill plus per-tile diagnostics (each nullable):
+ *  tile_state uint8 [B, H_q, M, M] (M = N / bm): BSFA_TILE_* of every tile
+ *  tile_max   fp32  [B, H_q, M, M]: the gate's s_max (maximum scaled score over
+ *             the visible entries) of every computed tile, NaN where not computed.
+ * Same contract as bsfa_prefill otherwise.  Slower: for testing and
+ * calibration, not for production.
+ */
+int bsfa_prefill_ex(const void* q, const void* k, const void* v, float* out, float* lse, int32_t* skip_counts,
+                    const float* thresholds, bsfa_shape shape, int causal, bsfa_block block,
+                    uint8_t* tile_state, float* tile_max, void* stream);
+
+/*
+ * bsfa_tile_max - calibration pass: the tile maxima alone.
+ *  q, k      as for bsfa_prefill
+ *  tile_max  fp32 [B, H_q, M, M]: max over the visible entries of each computed
+ *            tile of the scaled scores S = Q K^T / sqrt(d), NaN where a tile is
+ *            not computed (causal, j > i).  Bit-identical to the tile_max output
+ *            of bsfa_prefill_ex on the same inputs.
+ * This is the measurement the threshold calibration of Sec. 4.2 sorts: "the
+ * off-diagonal blocks ordered by their maximum scores".  QK^T only: no V is
+ * read, nothing else is written.  shape.thr_len is not used (must be >= 1).
+ */
+int bsfa_tile_max(const void* q, const void* k, float* tile_max, bsfa_shape shape, int causal, bsfa_block block,
+                  void* stream);
+
+/*
+ * bsfa_calibrate_fixed_k - fixed-k threshold table from tile maxima
+ * (Sec. 4.2; App. B.3 "Threshold tensor").
+ *  tile_max    fp32 [S, H, M, M] device: tile maxima of S calibration samples
+ *              (e.g. the batch of a bsfa_tile_max call), NaN-free on computed
+ *              tiles
+ *  thresholds  fp32 [H, M] device, written: for query block i with n_i
+ *              off-diagonal computed tiles (causal: i; bidirectional: M - 1),
+ *              -inf if n_i <= k, +inf if k == 0, otherwise the midpoint of the
+ *              k-th and (k+1)-th largest off-diagonal maxima, averaged over the
+ *              S samples.  With S = 1 and distinct maxima, bsfa_prefill with
+ *              this table keeps exactly min(k, n_i) off-diagonal tiles of every
+ *              query block.  Use with shape.thr_len = M.
+ * Errors: BSFA_ERR_SHAPE (counts < 1, k < 0), BSFA_ERR_UNSUPPORTED (M > 16384).
+ */
+int bsfa_calibrate_fixed_k(const float* tile_max, int64_t n_samples, int64_t n_heads, int64_t n_blocks, int causal,
+                           int64_t k, float* thresholds, void* stream);
+
+/*
+ * bsfa_validate - host-only check of a shape / mask / tile combination.
+ * Makes no HIP call.  Returns BSFA_OK if bsfa_prefill would accept it
+ * (pointer checks aside).
+ */
+int bsfa_validate(bsfa_shape shape, int causal, bsfa_block block);
+
+/* bsfa_status_string - static, human-readable text for a status code. */
+const char* bsfa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSFA_H */

@@ -61,6 +61,7 @@ __all__ = [
     "run_blocks",
     "run",
     "tile_maxima",
+    "calibrate_row",
     "calibrate_fixed_k",
     "STATE_PRUNED",
     "STATE_KEPT",
@@ -263,31 +264,38 @@ def tile_maxima(q, k, causal: bool, block: int, heads: Optional[Sequence[int]] =
     return out
 
 
-def calibrate_fixed_k(tile_max: np.ndarray, k: int, causal: bool) -> np.ndarray:
-    """Fixed-k thresholds [H_q, M] from sample tile maxima [S, H_q, M, M] (Sec. 4.2, App. B.3).
+def calibrate_row(tile_max_row: np.ndarray, i: int, k: int, causal: bool) -> float:
+    """Fixed-k threshold of query block i from one sample's tile maxima row [M] (Sec. 4.2).
 
-    Per sample, head and query block i: the off-diagonal computed tiles are
-    sorted by their maxima (largest first).  With n_i of them, the threshold
-    is -inf if n_i <= k, else the midpoint of the k-th and (k+1)-th largest
-    (+inf for k = 0), so that (barring ties) exactly the top k are retained.
-    The thresholds of the samples are then averaged.
+    The off-diagonal computed tiles (causal: j < i; bidirectional: j != i) are
+    sorted by their maxima, largest first.  With n of them: -inf if n <= k,
+    +inf if k == 0 (no off-diagonal tile retained), otherwise the midpoint of
+    the k-th and (k+1)-th largest, so that (barring ties) exactly the top k
+    are retained.
     """
     if k < 0:
         raise ValueError("k must be >= 0")
+    M = tile_max_row.shape[0]
+    cols = [j for j in (range(i) if causal else range(M)) if j != i]
+    if len(cols) <= k:
+        return -np.inf
+    if k == 0:
+        return np.inf
+    vals = np.sort(tile_max_row[cols])[::-1]
+    if np.isnan(vals).any():
+        raise ValueError("tile maxima missing for a calibrated row")
+    return 0.5 * (vals[k - 1] + vals[k])
+
+
+def calibrate_fixed_k(tile_max: np.ndarray, k: int, causal: bool) -> np.ndarray:
+    """Fixed-k thresholds [H_q, M] from sample tile maxima [S, H_q, M, M] (Sec. 4.2, App. B.3).
+
+    Each (head, query block) gets ``calibrate_row`` per sample; the samples'
+    thresholds are then averaged ("averaging across calibration samples").
+    """
     S, Hq, M, _ = tile_max.shape
     thr = np.zeros((Hq, M))
     for h in range(Hq):
         for i in range(M):
-            cols = [j for j in (range(i) if causal else range(M)) if j != i]
-            if len(cols) <= k:
-                thr[h, i] = -np.inf
-                continue
-            acc = 0.0
-            for s_idx in range(S):
-                vals = np.sort(tile_max[s_idx, h, i, cols])[::-1]
-                if np.isnan(vals).any():
-                    raise ValueError("tile maxima missing for a calibrated row")
-                # k = 0 retains no off-diagonal tile: a threshold above every maximum
-                acc += 0.5 * (vals[k - 1] + vals[k]) if k > 0 else np.inf
-            thr[h, i] = acc / S
+            thr[h, i] = sum(calibrate_row(tile_max[s_idx, h, i], i, k, causal) for s_idx in range(S)) / S
     return thr

@@ -1,0 +1,134 @@
+"""Helpers shared by the parity tests: threshold construction from the oracle
+and comparison of the HIP path's results with the oracle's.
+
+Acceptance (per tile / element, on identical bf16 inputs):
+  * skip mask identical, except tiles whose oracle s_max lies within 1e-3 of
+    the threshold (either decision is correct there);
+  * out: max |diff| <= 1e-2 and mean |diff| <= 1e-3;
+  * lse: max |diff| <= 1e-3;
+  * skip_counts equal to the number of skipped tiles of the same run;
+  * tile_max (diagnostic): |diff| <= 1e-4 + 1e-5 |s_max| (fp32 accumulation of
+    exact bf16 products against float64).
+Thresholds built by ``margin_thresholds`` keep every tile maximum at least
+2e-3 away, so on those inputs the mask must match exactly.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+OUT_MAX = 1e-2
+OUT_MEAN = 1e-3
+LSE_MAX = 1e-3
+EXEMPT = 1e-3
+TMAX_ABS = 1e-4
+TMAX_REL = 1e-5
+
+
+def away_from(t0: float, vals: np.ndarray, margin: float = 2e-3) -> float:
+    """``t0`` if every value is more than ``margin`` away from it, else the
+    middle of the nearest gap between consecutive values (or beyond the ends)
+    that is wider than 2*margin."""
+    vals = np.sort(vals[np.isfinite(vals)])
+    if not np.isfinite(t0) or vals.size == 0 or np.min(np.abs(vals - t0)) > margin:
+        return t0
+    ext = np.concatenate(([vals[0] - 4 * margin], vals, [vals[-1] + 4 * margin]))
+    mids = 0.5 * (ext[:-1] + ext[1:])
+    cand = mids[(ext[1:] - ext[:-1]) > 2 * margin]
+    return float(cand[np.argmin(np.abs(cand - t0))])
+
+
+def margin_thresholds(tile_max: np.ndarray, k, causal: bool, margin: float = 2e-3) -> np.ndarray:
+    """Fixed-k thresholds [H, M] (float32) from oracle tile maxima [B, H, M, M].
+
+    Starts from the oracle's fixed-k calibration (averaged over the batch) and,
+    where a tile maximum of any batch element lies within ``margin`` of it,
+    moves the threshold to the middle of the nearest gap wider than
+    2*margin between consecutive off-diagonal maxima.  ``k=None`` gives -inf.
+    Rows with no finite tile maxima keep the calibrated value.
+    """
+    B, H, M, _ = tile_max.shape
+    if k is None:
+        return np.full((H, M), -np.inf, dtype=np.float32)
+    thr = oracle.calibrate_fixed_k(tile_max, k, causal)
+    out = thr.astype(np.float32)
+    for h in range(H):
+        for i in range(M):
+            cols = [j for j in (range(i) if causal else range(M)) if j != i]
+            out[h, i] = np.float32(away_from(float(out[h, i]), tile_max[:, h, i, cols].ravel(), margin))
+    return out
+
+
+def exempt_tiles(oracle_tile_max: np.ndarray, thresholds: np.ndarray) -> np.ndarray:
+    """[B, H, M, M] bool: off-diagonal computed tiles whose s_max is within EXEMPT of tau."""
+    B, H, M, _ = oracle_tile_max.shape
+    t_len = thresholds.shape[1]
+    tau = thresholds[:, np.minimum(np.arange(M), t_len - 1)].astype(np.float64)  # [H, M]
+    near = np.abs(oracle_tile_max - tau[None, :, :, None]) <= EXEMPT
+    near &= np.isfinite(oracle_tile_max)
+    near[..., np.arange(M), np.arange(M)] = False
+    return near
+
+
+def compare_blocks(gpu: dict, ref_blocks, block: int, thresholds: np.ndarray, label: str = ""):
+    """Compare GPU outputs (numpy, full arrays) with oracle ``run_blocks`` results.
+
+    Returns a dict of statistics.  Raises AssertionError on any violation.
+    """
+    errs = []
+    n_exempt = 0
+    worst = 0.0
+    abs_sum = 0.0
+    count = 0
+    lse_worst = 0.0
+    tmax_worst = 0.0
+    for r in ref_blocks:
+        b, h, i = r["b"], r["h"], r["i"]
+        sl = slice(i * block, (i + 1) * block)
+        computed = np.isfinite(r["tile_max"])
+        st_ref = r["tile_state"]
+        if "tile_state" in gpu:
+            st_gpu = gpu["tile_state"][b, h, i]
+            tau = float(thresholds[h, min(i, thresholds.shape[1] - 1)])
+            near = np.zeros_like(computed)
+            near[computed] = np.abs(r["tile_max"][computed] - tau) <= EXEMPT
+            near[i] = False
+            n_exempt += int(near.sum())
+            bad = (st_gpu != st_ref) & ~near
+            if bad.any():
+                errs.append(f"{label} (b={b},h={h},i={i}): tile_state differs at j={np.flatnonzero(bad)[:8]}")
+            skipped_gpu = int((st_gpu == oracle.STATE_SKIPPED).sum())
+            if int(gpu["skip_counts"][b, h, i]) != skipped_gpu:
+                errs.append(f"{label} (b={b},h={h},i={i}): skip_count {gpu['skip_counts'][b, h, i]} != "
+                            f"{skipped_gpu} skipped tiles")
+            tm = gpu["tile_max"][b, h, i]
+            if not np.array_equal(np.isnan(tm), ~computed):
+                errs.append(f"{label} (b={b},h={h},i={i}): tile_max NaN pattern differs")
+            d = np.abs(tm[computed] - r["tile_max"][computed])
+            tol = TMAX_ABS + TMAX_REL * np.abs(r["tile_max"][computed])
+            tmax_worst = max(tmax_worst, float(d.max()) if d.size else 0.0)
+            if (d > tol).any():
+                errs.append(f"{label} (b={b},h={h},i={i}): tile_max off by {d.max():.3g}")
+        elif int(gpu["skip_counts"][b, h, i]) != r["skip_count"]:
+            errs.append(f"{label} (b={b},h={h},i={i}): skip_count {gpu['skip_counts'][b, h, i]} != "
+                        f"{r['skip_count']}")
+        o = gpu["out"][b, h, sl].astype(np.float64)
+        diff = np.abs(o - r["out"])
+        worst = max(worst, float(diff.max()))
+        abs_sum += float(diff.sum())
+        count += diff.size
+        ld = np.abs(gpu["lse"][b, h, sl].astype(np.float64) - r["lse"])
+        lse_worst = max(lse_worst, float(ld.max()))
+    mean = abs_sum / max(count, 1)
+    if worst > OUT_MAX:
+        errs.append(f"{label}: out max-abs {worst:.3g} > {OUT_MAX}")
+    if mean > OUT_MEAN:
+        errs.append(f"{label}: out mean-abs {mean:.3g} > {OUT_MEAN}")
+    if lse_worst > LSE_MAX:
+        errs.append(f"{label}: lse max-abs {lse_worst:.3g} > {LSE_MAX}")
+    stats = {"out_max": worst, "out_mean": mean, "lse_max": lse_worst, "tile_max_max": tmax_worst,
+             "exempt": n_exempt, "blocks": len(ref_blocks)}
+    assert not errs, "\n".join(errs[:20]) + f"\nstats={stats}"
+    return stats

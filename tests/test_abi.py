@@ -1,0 +1,90 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+include/bsfa.h declares, validates shapes and rejects bad pointers before any
+HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_flashattention_tiled_amd import binding as bb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bb.LIB_PATH):
+        from block_sparse_flashattention_tiled_amd import build_lib
+
+        build_lib.build()
+    return bb.load_library()
+
+
+def _declared():
+    names = set()
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", f)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(bsfa_\w+)\s*\(", src))
+    return names
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared()
+    assert {"bsfa_prefill", "bsfa_prefill_ex", "bsfa_validate", "bsfa_status_string"} <= declared
+    for name in declared:
+        assert hasattr(lib, name), f"{name} declared but not exported"
+    assert set(bb.EXPORTED) <= declared
+
+
+def S(B=1, Hq=4, Hkv=2, N=1024, d=128, T=8):
+    return bb.make_shape(B, Hq, Hkv, N, d, T)
+
+
+@pytest.mark.parametrize(
+    "shape,causal,blk,status",
+    [
+        (S(), 1, 128, 0),
+        (S(d=64), 0, 64, 0),
+        (S(N=1000), 1, 128, 2),      # not a multiple of the tile
+        (S(Hq=3, Hkv=2), 1, 128, 2),  # H_q % H_kv
+        (S(d=96), 1, 128, 3),        # unsupported head dim
+        (S(), 1, 96, 3),             # unsupported tile
+        (S(), 2, 128, 2),            # causal flag
+        (S(T=0), 1, 128, 2),
+        (S(B=0), 1, 128, 2),
+        (S(N=-128), 1, 128, 2),
+    ],
+)
+def test_validate(lib, shape, causal, blk, status):
+    assert bb.bsfa_validate(shape, causal, bb.make_block(blk)) == status
+
+
+def test_rectangular_tile_unsupported(lib):
+    assert bb.bsfa_validate(S(), 1, bb.make_block(128, 64)) == 3
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert bb.status_string(s) and bb.status_string(s) != "unknown status"
+    assert bb.status_string(99) == "unknown status"
+
+
+def test_null_and_misaligned_pointers_rejected_before_any_launch(lib):
+    shape, blk = S(), bb.make_block(128)
+    f = lib.bsfa_prefill
+    good = 0x100000
+    # required pointer missing
+    assert f(None, good, good, good, None, None, good, shape, 1, blk, None) == 1
+    assert f(good, good, good, good, None, None, None, shape, 1, blk, None) == 1
+    # misaligned bf16 / fp32 buffers
+    assert f(good + 2, good, good, good, None, None, good, shape, 1, blk, None) == 4
+    assert f(good, good, good, good + 4, None, None, good, shape, 1, blk, None) == 4
+    assert f(good, good, good, good, good + 2, None, good, shape, 1, blk, None) == 4
+    # shape errors win over pointer errors
+    assert f(None, None, None, None, None, None, None, S(N=1000), 1, blk, None) == 2
+    assert lib.bsfa_prefill_ex(good, good, good, good, None, None, good, shape, 1, blk, None, good + 1,
+                               None) == 4
