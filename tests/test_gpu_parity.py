@@ -48,6 +48,13 @@ CASES = {
     "one-threshold-per-head": (dict(base="llama8k", seq_len=1024, heads_q=2, heads_kv=1), 3, "t_len1"),
     "table-shorter-than-M": (dict(base="llama8k", seq_len=2048, heads_q=2, heads_kv=1), 4, "t_len4"),
     "single-tile": (dict(base="llama8k", seq_len=128, heads_q=2, heads_kv=1), None, "+inf"),
+    # shapes that route to the one-unit-per-workgroup kernel (odd group, causal;
+    # bidirectional with an odd number of blocks) and to block pairs (odd group, bidirectional)
+    "odd-group-causal": (dict(base="llama8k", seq_len=1024, heads_q=3, heads_kv=1), 3, "calib"),
+    "odd-group-bidirectional-even-M": (dict(base="llama8k", seq_len=1024, heads_q=3, heads_kv=1, causal=False), 2,
+                                       "calib"),
+    "bidirectional-odd-M": (dict(base="dit32k", batch=1, heads_q=2, heads_kv=2, seq_len=896, grid=(4, 7, 32)), 2,
+                            "calib"),
 }
 
 
