@@ -110,6 +110,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle baseline budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="also run one plain 1 GiB device copy, whose HBM counters calibrate the kernel's")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -160,6 +162,14 @@ def main():
     def launch(pi):
         bb.bsfa_prefill(q, k, v, out, lse, counts[pi], points[pi]["thr"], shape, int(w.causal), block, stream)
 
+    if args.traffic_probe:
+        # a copy of known size: reads 1 GiB and writes 1 GiB; profiling counters
+        # taken in the same run are scaled by what this copy reports
+        a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
     log(f"warmup {args.warmup} steps x {len(points)} launches")
     for _ in range(args.warmup):
         for pi in range(len(points)):
