@@ -41,6 +41,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "bsfa_internal.h"
 
 namespace bsfa {
@@ -491,9 +493,13 @@ __global__ void __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2,
     *reinterpret_cast<u32x4*>(k_lds + (c / C::CPR) * C::KS + (c % C::CPR) * 16) = kreg[it];
   }
 
-  for (int j = 0; j <= jend; ++j) {
+  // One key tile.  DIAGC is true only for the causal diagonal tile, the last
+  // one visited, so the masking of keys after the query is compiled into that
+  // single step and not evaluated (or predicated) on every other tile.
+  auto step = [&](const int j, auto DIAGC) {
+    constexpr bool DIAG_TILE = decltype(DIAGC)::value;
     lds_barrier();  // (a): K_j (and Q) visible; every wave is done with V_{j-1}
-    const bool more = j < jend;
+    const bool more = CAUSAL ? !DIAG_TILE : (j < jend);
     if (more) {
       const u32x4* src = kg + (size_t)(j + 1) * TILE_CHUNKS;
 #pragma unroll
@@ -502,8 +508,7 @@ __global__ void __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2,
     // ---- (a4) S^T = K_j Q^T ------------------------------------------------
     f32x16 s[C::KB];
     qk_tile_qlds<D, BLK>(s, k_lds, k_lane, q_lds[u], q_lane);
-    const bool diag = (j == i);
-    if (CAUSAL && diag) {
+    if constexpr (CAUSAL && DIAG_TILE) {
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
@@ -617,6 +622,12 @@ __global__ void __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2,
           }
       }
     }
+  };
+  if constexpr (CAUSAL) {
+    for (int j = 0; j < i; ++j) step(j, std::false_type{});
+    step(i, std::true_type{});
+  } else {
+    for (int j = 0; j <= jend; ++j) step(j, std::false_type{});
   }
 
   const int utid = wu * 64 + lane;  // thread index inside the unit
