@@ -21,12 +21,17 @@ LIB_PATH = os.path.join(_PKG, "libbsfa.so")
 
 BSFA_OK = 0
 TILE_PRUNED, TILE_KEPT, TILE_SKIPPED, TILE_DIAGONAL = 0, 1, 2, 3
+GATE_THRESHOLD, GATE_GAP = 0, 1
+GATES = {"threshold": GATE_THRESHOLD, "gap": GATE_GAP}
 
 EXPORTED = (
     "bsfa_prefill",
     "bsfa_prefill_ex",
+    "bsfa_prefill_bf16",
+    "bsfa_prefill_gated",
     "bsfa_tile_max",
     "bsfa_calibrate_fixed_k",
+    "bsfa_calibrate_levels",
     "bsfa_validate",
     "bsfa_status_string",
 )
@@ -67,14 +72,19 @@ def load_library() -> ctypes.CDLL:
             "`python -m block_sparse_flashattention_tiled_amd.build_lib` (there is no fallback path)"
         )
     lib = ctypes.CDLL(LIB_PATH)
-    vp, i32, i64p = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     lib.bsfa_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, BsfaShape, i32, BsfaBlock, vp]
     lib.bsfa_prefill.restype = i32
     lib.bsfa_prefill_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, BsfaShape, i32, BsfaBlock, vp, vp, vp]
     lib.bsfa_prefill_ex.restype = i32
+    lib.bsfa_prefill_bf16.argtypes = [vp, vp, vp, vp, vp, vp, vp, BsfaShape, i32, BsfaBlock, vp]
+    lib.bsfa_prefill_bf16.restype = i32
+    lib.bsfa_prefill_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, BsfaShape, i32, BsfaBlock, i32, vp, vp, vp]
+    lib.bsfa_prefill_gated.restype = i32
+    lib.bsfa_calibrate_levels.argtypes = [vp, i64, i64, i64, i32, vp, i64, vp, vp]
+    lib.bsfa_calibrate_levels.restype = i32
     lib.bsfa_tile_max.argtypes = [vp, vp, vp, BsfaShape, i32, BsfaBlock, vp]
     lib.bsfa_tile_max.restype = i32
-    i64 = ctypes.c_int64
     lib.bsfa_calibrate_fixed_k.argtypes = [vp, i64, i64, i64, i32, i64, vp, vp]
     lib.bsfa_calibrate_fixed_k.restype = i32
     lib.bsfa_validate.argtypes = [BsfaShape, i32, BsfaBlock]
@@ -127,7 +137,8 @@ def _check(t, name, dtype, shape, device):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
-def _check_all(q, k, v, out, lse, skip_counts, thresholds, shape, block, tile_state=None, tile_max=None):
+def _check_all(q, k, v, out, lse, skip_counts, thresholds, shape, block, tile_state=None, tile_max=None,
+               out_dtype=torch.float32):
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("tensors must live on the GPU")
@@ -137,7 +148,7 @@ def _check_all(q, k, v, out, lse, skip_counts, thresholds, shape, block, tile_st
     _check(q, "q", torch.bfloat16, (B, Hq, N, d), dev)
     _check(k, "k", torch.bfloat16, (B, Hkv, N, d), dev)
     _check(v, "v", torch.bfloat16, (B, Hkv, N, d), dev)
-    _check(out, "out", torch.float32, (B, Hq, N, d), dev)
+    _check(out, "out", out_dtype, (B, Hq, N, d), dev)
     _check(lse, "lse", torch.float32, (B, Hq, N), dev)
     _check(skip_counts, "skip_counts", torch.int32, (B, Hq, M), dev)
     _check(thresholds, "thresholds", torch.float32, (Hq, T), dev)
@@ -171,6 +182,50 @@ def bsfa_prefill_ex(q, k, v, out, lse, skip_counts, thresholds, shape: BsfaShape
         shape, int(causal), block, _ptr(tile_state), _ptr(tile_max), _stream(stream))
     if st != BSFA_OK:
         raise BsfaError(st, "bsfa_prefill_ex")
+
+
+def bsfa_prefill_bf16(q, k, v, out, lse, skip_counts, thresholds, shape: BsfaShape, causal: int,
+                      block: BsfaBlock, stream=None) -> None:
+    """C ABI ``bsfa_prefill_bf16`` on torch tensors: ``out`` is bf16 (see include/bsfa.h)."""
+    st = bsfa_validate(shape, causal, block)
+    if st != BSFA_OK:
+        raise BsfaError(st, "bsfa_prefill_bf16")
+    _check_all(q, k, v, out, lse, skip_counts, thresholds, shape, block, out_dtype=torch.bfloat16)
+    st = load_library().bsfa_prefill_bf16(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(skip_counts), _ptr(thresholds),
+        shape, int(causal), block, _stream(stream))
+    if st != BSFA_OK:
+        raise BsfaError(st, "bsfa_prefill_bf16")
+
+
+def bsfa_prefill_gated(q, k, v, out, lse, skip_counts, thresholds, shape: BsfaShape, causal: int,
+                       block: BsfaBlock, gate: int, tile_state=None, tile_max=None, stream=None) -> None:
+    """C ABI ``bsfa_prefill_gated`` on torch tensors (see include/bsfa.h)."""
+    st = bsfa_validate(shape, causal, block)
+    if st != BSFA_OK:
+        raise BsfaError(st, "bsfa_prefill_gated")
+    _check_all(q, k, v, out, lse, skip_counts, thresholds, shape, block, tile_state, tile_max)
+    st = load_library().bsfa_prefill_gated(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(skip_counts), _ptr(thresholds),
+        shape, int(causal), block, int(gate), _ptr(tile_state), _ptr(tile_max), _stream(stream))
+    if st != BSFA_OK:
+        raise BsfaError(st, "bsfa_prefill_gated")
+
+
+def bsfa_calibrate_levels(tile_max, n_samples: int, n_heads: int, n_blocks: int, causal: int, ks,
+                          thresholds, stream=None) -> None:
+    """C ABI ``bsfa_calibrate_levels``: ``ks`` is a host sequence of ints, ``thresholds``
+    a [len(ks), H, M] fp32 device tensor (see include/bsfa.h)."""
+    dev = tile_max.device
+    ks = [int(x) for x in ks]
+    _check(tile_max, "tile_max", torch.float32, (n_samples, n_heads, n_blocks, n_blocks), dev)
+    _check(thresholds, "thresholds", torch.float32, (len(ks), n_heads, n_blocks), dev)
+    arr = (ctypes.c_int64 * max(len(ks), 1))(*ks)
+    st = load_library().bsfa_calibrate_levels(_ptr(tile_max), n_samples, n_heads, n_blocks, int(causal),
+                                              ctypes.cast(arr, ctypes.c_void_p), len(ks), _ptr(thresholds),
+                                              _stream(stream))
+    if st != BSFA_OK:
+        raise BsfaError(st, "bsfa_calibrate_levels")
 
 
 def bsfa_tile_max(q, k, tile_max, shape: BsfaShape, causal: int, block: BsfaBlock, stream=None) -> None:
@@ -221,10 +276,22 @@ def calibrate_fixed_k(tile_maxima: torch.Tensor, k: Optional[int], causal: bool,
     return thr
 
 
-def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, thresholds: torch.Tensor, causal: bool,
-            block: int, diagnostics: bool = False, stream=None) -> dict:
-    """Allocate the outputs and run ``bsfa_prefill`` (or ``_ex`` with diagnostics).
+def calibrate_levels(tile_maxima: torch.Tensor, ks, causal: bool, stream=None) -> torch.Tensor:
+    """Threshold tensor [len(ks), H, M]: one fixed-k table per sparsity level."""
+    S, H, M, _ = tile_maxima.shape
+    thr = torch.empty((len(ks), H, M), dtype=torch.float32, device=tile_maxima.device)
+    bsfa_calibrate_levels(tile_maxima, S, H, M, int(causal), ks, thr, stream)
+    return thr
 
+
+def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, thresholds: torch.Tensor, causal: bool,
+            block: int, diagnostics: bool = False, stream=None, gate: str = "threshold",
+            out_dtype: torch.dtype = torch.float32) -> dict:
+    """Allocate the outputs and run the forward pass.
+
+    ``bsfa_prefill`` by default; ``bsfa_prefill_ex`` with diagnostics;
+    ``bsfa_prefill_gated`` for ``gate="gap"``; ``bsfa_prefill_bf16`` for a
+    bf16 output (threshold gate, no diagnostics).
     q: bf16 [B, H_q, N, d]; k, v: bf16 [B, H_kv, N, d]; thresholds: fp32 [H_q, T_len].
     Returns a dict of device tensors: out, lse, skip_counts (+ tile_state, tile_max).
     """
@@ -234,11 +301,28 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, thresholds: torch
     blk = make_block(block)
     M = N // block
     dev = q.device
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    if gate not in GATES:
+        raise ValueError(f"gate must be one of {sorted(GATES)}")
     res = {
-        "out": torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev),
+        "out": torch.empty((B, Hq, N, d), dtype=out_dtype, device=dev),
         "lse": torch.empty((B, Hq, N), dtype=torch.float32, device=dev),
         "skip_counts": torch.empty((B, Hq, M), dtype=torch.int32, device=dev),
     }
+    if out_dtype == torch.bfloat16:
+        if diagnostics or gate != "threshold":
+            raise ValueError("the bf16 output entry point has the threshold gate and no diagnostics")
+        bsfa_prefill_bf16(q, k, v, res["out"], res["lse"], res["skip_counts"], thresholds, shape, int(causal), blk,
+                          stream)
+        return res
+    if gate != "threshold":
+        if diagnostics:
+            res["tile_state"] = torch.empty((B, Hq, M, M), dtype=torch.uint8, device=dev)
+            res["tile_max"] = torch.empty((B, Hq, M, M), dtype=torch.float32, device=dev)
+        bsfa_prefill_gated(q, k, v, res["out"], res["lse"], res["skip_counts"], thresholds, shape, int(causal),
+                           blk, GATES[gate], res.get("tile_state"), res.get("tile_max"), stream)
+        return res
     if diagnostics:
         res["tile_state"] = torch.empty((B, Hq, M, M), dtype=torch.uint8, device=dev)
         res["tile_max"] = torch.empty((B, Hq, M, M), dtype=torch.float32, device=dev)

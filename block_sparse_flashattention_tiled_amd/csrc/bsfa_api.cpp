@@ -48,13 +48,16 @@ bsfa::FwdParams shape_params(const bsfa_shape& shape, const bsfa_block& block) {
   return p;
 }
 
-int prefill_impl(const void* q, const void* k, const void* v, float* out, float* lse, int32_t* skip_counts,
-                 const float* thresholds, bsfa_shape shape, int causal, bsfa_block block, uint8_t* tile_state,
-                 float* tile_max, int diagnostics, void* stream) {
+// out is fp32 unless out_bf16 is set (then out is null)
+int prefill_impl(const void* q, const void* k, const void* v, float* out, uint16_t* out_bf16, float* lse,
+                 int32_t* skip_counts, const float* thresholds, bsfa_shape shape, int causal, bsfa_block block,
+                 int gate, uint8_t* tile_state, float* tile_max, int diagnostics, void* stream) {
   const int st = check_shape(shape, causal, block);
   if (st != BSFA_OK) return st;
-  if (!q || !k || !v || !out || !thresholds) return BSFA_ERR_NULL;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return BSFA_ERR_ALIGN;
+  if (gate != BSFA_GATE_THRESHOLD && gate != BSFA_GATE_GAP) return BSFA_ERR_SHAPE;
+  if (!q || !k || !v || !(out || out_bf16) || !thresholds) return BSFA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out ? (const void*)out : out_bf16, 16))
+    return BSFA_ERR_ALIGN;
   if (!aligned(thresholds, 4) || (lse && !aligned(lse, 4)) || (skip_counts && !aligned(skip_counts, 4)) ||
       (tile_max && !aligned(tile_max, 4)))
     return BSFA_ERR_ALIGN;
@@ -64,6 +67,8 @@ int prefill_impl(const void* q, const void* k, const void* v, float* out, float*
   p.k = static_cast<const uint16_t*>(k);
   p.v = static_cast<const uint16_t*>(v);
   p.out = out;
+  p.out_bf16 = out_bf16;
+  p.gate = gate;
   p.lse = lse;
   p.skip_counts = skip_counts;
   p.thresholds = thresholds;
@@ -93,15 +98,29 @@ const char* bsfa_status_string(int status) {
 
 int bsfa_prefill(const void* q, const void* k, const void* v, float* out, float* lse, int32_t* skip_counts,
                  const float* thresholds, bsfa_shape shape, int causal, bsfa_block block, void* stream) {
-  return prefill_impl(q, k, v, out, lse, skip_counts, thresholds, shape, causal, block, nullptr, nullptr, 0,
-                      stream);
+  return prefill_impl(q, k, v, out, nullptr, lse, skip_counts, thresholds, shape, causal, block,
+                      BSFA_GATE_THRESHOLD, nullptr, nullptr, 0, stream);
 }
 
 int bsfa_prefill_ex(const void* q, const void* k, const void* v, float* out, float* lse, int32_t* skip_counts,
                     const float* thresholds, bsfa_shape shape, int causal, bsfa_block block, uint8_t* tile_state,
                     float* tile_max, void* stream) {
-  return prefill_impl(q, k, v, out, lse, skip_counts, thresholds, shape, causal, block, tile_state, tile_max, 1,
-                      stream);
+  return prefill_impl(q, k, v, out, nullptr, lse, skip_counts, thresholds, shape, causal, block,
+                      BSFA_GATE_THRESHOLD, tile_state, tile_max, 1, stream);
+}
+
+int bsfa_prefill_bf16(const void* q, const void* k, const void* v, void* out, float* lse, int32_t* skip_counts,
+                      const float* thresholds, bsfa_shape shape, int causal, bsfa_block block, void* stream) {
+  return prefill_impl(q, k, v, nullptr, static_cast<uint16_t*>(out), lse, skip_counts, thresholds, shape, causal,
+                      block, BSFA_GATE_THRESHOLD, nullptr, nullptr, 0, stream);
+}
+
+int bsfa_prefill_gated(const void* q, const void* k, const void* v, float* out, float* lse, int32_t* skip_counts,
+                       const float* thresholds, bsfa_shape shape, int causal, bsfa_block block, int gate,
+                       uint8_t* tile_state, float* tile_max, void* stream) {
+  const int diagnostics = (tile_state || tile_max) ? 1 : 0;
+  return prefill_impl(q, k, v, out, nullptr, lse, skip_counts, thresholds, shape, causal, block, gate, tile_state,
+                      tile_max, diagnostics, stream);
 }
 
 int bsfa_tile_max(const void* q, const void* k, float* tile_max, bsfa_shape shape, int causal, bsfa_block block,
@@ -128,6 +147,27 @@ int bsfa_calibrate_fixed_k(const float* tile_max, int64_t n_samples, int64_t n_h
   const int kk = (int)(k < n_blocks ? k : n_blocks);
   return bsfa::launch_calibrate(tile_max, (int)n_samples, (int)n_heads, (int)n_blocks, causal, kk, thresholds,
                                 static_cast<hipStream_t>(stream));
+}
+
+int bsfa_calibrate_levels(const float* tile_max, int64_t n_samples, int64_t n_heads, int64_t n_blocks, int causal,
+                          const int64_t* ks, int64_t n_levels, float* thresholds, void* stream) {
+  if (n_samples < 1 || n_heads < 1 || n_blocks < 1 || n_levels < 1 || (causal != 0 && causal != 1))
+    return BSFA_ERR_SHAPE;
+  if (!ks || !tile_max || !thresholds) return BSFA_ERR_NULL;
+  for (int64_t l = 0; l < n_levels; ++l)
+    if (ks[l] < 0) return BSFA_ERR_SHAPE;
+  if (n_blocks > bsfa::kCalibMaxBlocks) return BSFA_ERR_UNSUPPORTED;
+  if (n_heads * n_blocks > INT32_MAX || n_samples > INT32_MAX || n_levels > INT32_MAX / (n_heads * n_blocks))
+    return BSFA_ERR_SHAPE;
+  if (!aligned(tile_max, 4) || !aligned(thresholds, 4)) return BSFA_ERR_ALIGN;
+  const int64_t level_size = n_heads * n_blocks;
+  for (int64_t l = 0; l < n_levels; ++l) {
+    const int kk = (int)(ks[l] < n_blocks ? ks[l] : n_blocks);
+    const int st = bsfa::launch_calibrate(tile_max, (int)n_samples, (int)n_heads, (int)n_blocks, causal, kk,
+                                          thresholds + l * level_size, static_cast<hipStream_t>(stream));
+    if (st != BSFA_OK) return st;
+  }
+  return BSFA_OK;
 }
 
 }  // extern "C"

@@ -87,6 +87,56 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Gate of one query unit for tile j (a5).  Threshold gate (the pages'
+// method, "Block Sparse Flash Attention" Sec. 4.1 and 4.4): an off-diagonal
+// tile is skipped iff s_max < tau, strictly.  Gap gate (the comparison
+// reference of BLASST and of SpargeAttention's in-kernel P.V skip, Sec. 3
+// "Related Work": a tile far below the running maximum): skipped iff
+// s_max < M - tau, where M is the largest s_max among the unit's tiles kept so
+// far.  Both compare in the scaled-score domain; NaN compares false (kept).
+__device__ __forceinline__ int gate_skip(int gap, bool off_diag, float tms, float tau, float& mrun) {
+  const float ref = gap ? mrun - tau : tau;
+  const int skip = (off_diag && tms < ref) ? 1 : 0;
+  if (!skip) mrun = fmaxf(mrun, tms);
+  return skip;
+}
+
+// (a9) one lane's share of an output row O = O_acc / l: four runs of four
+// consecutive columns per 32-column block, fp32, or rounded to bf16 (nearest
+// even) when the caller asked for a bf16 output.
+template <int DB>
+__device__ __forceinline__ void store_out_row(const FwdParams& p, size_t row, const f32x16 (&o)[DB], float inv,
+                                              int hh) {
+  constexpr int D = DB * 32;
+  if (p.out_bf16) {
+    uint16_t* ob = p.out_bf16 + row * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x2 lo = {o[db][4 * g4 + 0] * inv, o[db][4 * g4 + 1] * inv};
+        const f32x2 hi = {o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv};
+        uint2 val;
+        val.x = __builtin_bit_cast(unsigned, __builtin_convertvector(lo, bf16x2));
+        val.y = __builtin_bit_cast(unsigned, __builtin_convertvector(hi, bf16x2));
+        *reinterpret_cast<uint2*>(ob + db * 32 + 8 * g4 + 4 * hh) = val;
+      }
+    return;
+  }
+  float* og = p.out + row * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      float4 val;
+      val.x = o[db][4 * g4 + 0] * inv;
+      val.y = o[db][4 * g4 + 1] * inv;
+      val.z = o[db][4 * g4 + 2] * inv;
+      val.w = o[db][4 * g4 + 3] * inv;
+      *reinterpret_cast<float4*>(og + db * 32 + 8 * g4 + 4 * hh) = val;
+    }
+}
+
 // S^T = K_j Q_i^T for this wave's 32 query rows.
 // s[kb][r] = raw score of query row (lane % 32) and key kb*32 + 8(r/4) + 4(lane/32) + r%4.
 template <int D, int BLK, int NKB, int NKC>
@@ -178,6 +228,7 @@ __global__ void __launch_bounds__(BLK * 2) bsfa_fwd_kernel(const FwdParams p) {
   float m_run = -INFINITY;  // reference max of O and l, in units of scale*log2(e)
   float l_run = 0.f;        // sum of exp over this lane's half of the keys (for lse)
   float lb_run = 0.f;       // the same sum over the bf16-rounded P~ (normalises O)
+  float mrun = -INFINITY;   // largest s_max of the kept tiles (gap gate)
   int nskip = 0;
 
   // K_0 -> LDS
@@ -233,7 +284,7 @@ __global__ void __launch_bounds__(BLK * 2) bsfa_fwd_kernel(const FwdParams p) {
 #pragma unroll
     for (int ww = 1; ww < C::NW; ++ww) tm = fmaxf(tm, red[ww]);
     const float tms = tm * p.scale;  // s_max in the scaled-score domain
-    int skip = (MAXONLY || (!diag && tms < tau)) ? 1 : 0;
+    int skip = MAXONLY ? 1 : gate_skip(p.gate, !diag, tms, tau, mrun);
     skip = __builtin_amdgcn_readfirstlane(skip);
     if (DIAG_OUT && tid == 0) {
       if (p.tile_state) p.tile_state[diag_row + j] = diag ? 3 : (skip ? 2 : 1);
@@ -329,18 +380,7 @@ __global__ void __launch_bounds__(BLK * 2) bsfa_fwd_kernel(const FwdParams p) {
   // ---- (a9) epilogue: O_i = O_acc / l, lse, skip count -------------------
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.f / (lb_run + __shfl_xor(lb_run, 32));
-  float* og = p.out + (q_head + qrow) * D;
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      float4 val;
-      val.x = o[db][4 * g4 + 0] * inv;
-      val.y = o[db][4 * g4 + 1] * inv;
-      val.z = o[db][4 * g4 + 2] * inv;
-      val.w = o[db][4 * g4 + 3] * inv;
-      *reinterpret_cast<float4*>(og + db * 32 + 8 * g4 + 4 * hh) = val;
-    }
+  store_out_row(p, q_head + qrow, o, inv, hh);
   if (p.lse && hh == 0) p.lse[q_head + qrow] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
   if (p.skip_counts && tid == 0) p.skip_counts[(size_t)(b * p.Hq + hq) * p.M + i] = nskip;
   if (DIAG_OUT && CAUSAL) {
@@ -481,6 +521,7 @@ __global__ void __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2,
   float m_run = -INFINITY;
   float l_run = 0.f;
   float lb_run = 0.f;
+  float mrun_u[2] = {-INFINITY, -INFINITY};  // per unit: largest s_max of its kept tiles (gap gate)
   int nskip = 0;
 
   u32x4 kreg[P2::LD];
@@ -540,7 +581,7 @@ __global__ void __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
       for (int ww = 1; ww < P2::NWU; ++ww) tm = fmaxf(tm, red[uu][ww]);
       const float tms = tm * p.scale;
-      skip_of[uu] = (MAXONLY || (j != i_u[uu] && tms < tau_u[uu])) ? 1 : 0;
+      skip_of[uu] = MAXONLY ? 1 : gate_skip(p.gate, j != i_u[uu], tms, tau_u[uu], mrun_u[uu]);
       if (DIAG_OUT && uu == u && wu == 0 && lane == 0) {
         if (p.tile_state) p.tile_state[diag_row + j] = (j == i) ? 3 : (skip_of[uu] ? 2 : 1);
         if (p.tile_max) p.tile_max[diag_row + j] = tms;
@@ -640,18 +681,7 @@ __global__ void __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2,
   // ---- (a9) epilogue -------------------------------------------------------
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.f / (lb_run + __shfl_xor(lb_run, 32));
-  float* og = p.out + (q_head + qrow) * D;
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      float4 val;
-      val.x = o[db][4 * g4 + 0] * inv;
-      val.y = o[db][4 * g4 + 1] * inv;
-      val.z = o[db][4 * g4 + 2] * inv;
-      val.w = o[db][4 * g4 + 3] * inv;
-      *reinterpret_cast<float4*>(og + db * 32 + 8 * g4 + 4 * hh) = val;
-    }
+  store_out_row(p, q_head + qrow, o, inv, hh);
   if (p.lse && hh == 0) p.lse[q_head + qrow] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
   if (p.skip_counts && utid == 0) p.skip_counts[(size_t)(b * p.Hq + hq) * p.M + i] = nskip;
   if (DIAG_OUT && CAUSAL) {

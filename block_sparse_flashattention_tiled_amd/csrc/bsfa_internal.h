@@ -11,7 +11,8 @@ struct FwdParams {
   const uint16_t* q;  // bf16 [B, Hq, N, d]
   const uint16_t* k;  // bf16 [B, Hkv, N, d]
   const uint16_t* v;  // bf16 [B, Hkv, N, d]
-  float* out;         // fp32 [B, Hq, N, d]
+  float* out;         // fp32 [B, Hq, N, d] (unless out_bf16 is set)
+  uint16_t* out_bf16; // bf16 [B, Hq, N, d] or null: the output in bf16 instead of fp32
   float* lse;         // fp32 [B, Hq, N] or null
   int32_t* skip_counts;     // int32 [B, Hq, M] or null
   const float* thresholds;  // fp32 [Hq, T_len]
@@ -21,6 +22,7 @@ struct FwdParams {
   float scale;       // 1 / sqrt(d)
   float scale_log2;  // scale * log2(e)
   int remap;         // 1: XCD-aware workgroup order applies (grid % (8 * G) == 0)
+  int gate;          // 0: threshold gate (s_max < tau); 1: gap gate (s_max < running max - tau)
 };
 
 // Enqueue the forward kernel; mode 0 = forward, 1 = forward with per-tile

@@ -66,6 +66,17 @@ enum {
   BSFA_ERR_LAUNCH = 5       /* the HIP runtime refused the launch */
 };
 
+/* Gates of bsfa_prefill_gated.  Both compare a tile's s_max (maximum scaled
+ * score over its visible entries) in the scaled-score domain; diagonal tiles
+ * always pass; NaN comparisons keep the tile. */
+enum {
+  BSFA_GATE_THRESHOLD = 0, /* the pages' gate (Sec. 4.1, 4.4): skip iff s_max < tau */
+  BSFA_GATE_GAP = 1        /* skip iff s_max < M - tau, M = largest s_max of the tiles of
+                              this (head, query block) kept so far, in key-block order:
+                              the running-maximum comparison of BLASST and of
+                              SpargeAttention's in-kernel P.V skip (Sec. 3 "Related Work") */
+};
+
 /* Tile states written by bsfa_prefill_ex. */
 enum {
   BSFA_TILE_PRUNED = 0,   /* causal: above the diagonal, never computed */
@@ -114,6 +125,33 @@ int bsfa_prefill_ex(const void* q, const void* k, const void* v, float* out, flo
                     uint8_t* tile_state, float* tile_max, void* stream);
 
 /*
+ * bsfa_prefill_bf16 - bsfa_prefill writing the output in bf16: out is
+ * bf16 [B, H_q, N, d] (16-byte aligned), each element the fp32 result of
+ * bsfa_prefill rounded to nearest even.  Lets the call replace an attention
+ * whose output is consumed in bf16 ("drop-in replacement", Sec. 1) without a
+ * separate conversion pass.  lse stays fp32.  Same contract otherwise.
+ */
+int bsfa_prefill_bf16(const void* q, const void* k, const void* v, void* out, float* lse, int32_t* skip_counts,
+                      const float* thresholds, bsfa_shape shape, int causal, bsfa_block block, void* stream);
+
+/*
+ * bsfa_prefill_gated - bsfa_prefill with a choice of gate and optional
+ * per-tile diagnostics.
+ *  gate        BSFA_GATE_THRESHOLD: identical to bsfa_prefill.
+ *              BSFA_GATE_GAP: thresholds[h, min(i, T_len-1)] is the gap tau;
+ *              key blocks are visited in increasing order and off-diagonal
+ *              tile j is skipped iff s_max(i, j) < M - tau, M the largest
+ *              s_max of the tiles kept before it (-inf before the first),
+ *              so the first visited tile is always kept.  tau = +inf keeps
+ *              everything.
+ *  tile_state, tile_max  as for bsfa_prefill_ex; both NULL = production launch.
+ * Errors as for bsfa_prefill, plus BSFA_ERR_SHAPE for an unknown gate.
+ */
+int bsfa_prefill_gated(const void* q, const void* k, const void* v, float* out, float* lse, int32_t* skip_counts,
+                       const float* thresholds, bsfa_shape shape, int causal, bsfa_block block, int gate,
+                       uint8_t* tile_state, float* tile_max, void* stream);
+
+/*
  * bsfa_tile_max - calibration pass: the tile maxima alone.
  *  q, k      as for bsfa_prefill
  *  tile_max  fp32 [B, H_q, M, M]: max over the visible entries of each computed
@@ -144,6 +182,22 @@ int bsfa_tile_max(const void* q, const void* k, float* tile_max, bsfa_shape shap
  */
 int bsfa_calibrate_fixed_k(const float* tile_max, int64_t n_samples, int64_t n_heads, int64_t n_blocks, int causal,
                            int64_t k, float* thresholds, void* stream);
+
+/*
+ * bsfa_calibrate_levels - the threshold tensor for several sparsity levels at
+ * once (App. B.3 "Threshold tensor": one table per sparsity level, the level
+ * chosen at inference time by selecting its slice).
+ *  tile_max    as for bsfa_calibrate_fixed_k
+ *  ks          HOST array of n_levels values of k (each >= 0)
+ *  thresholds  fp32 [n_levels, H, M] device, written: slice l is exactly what
+ *              bsfa_calibrate_fixed_k returns for k = ks[l].  Pass
+ *              thresholds + l * H * M (with shape.thr_len = M) to bsfa_prefill
+ *              to run at level l.
+ * Errors: as bsfa_calibrate_fixed_k, BSFA_ERR_NULL for ks == NULL,
+ * BSFA_ERR_SHAPE for n_levels < 1 or a negative k.
+ */
+int bsfa_calibrate_levels(const float* tile_max, int64_t n_samples, int64_t n_heads, int64_t n_blocks, int causal,
+                          const int64_t* ks, int64_t n_levels, float* thresholds, void* stream);
 
 /*
  * bsfa_validate - host-only check of a shape / mask / tile combination.

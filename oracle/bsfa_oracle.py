@@ -37,6 +37,15 @@ the gate uses the scaled score; the tile max runs over visible entries only;
 GQA groups are contiguous (g = h // (H_q / H_kv)); lse is the natural log of
 the scaled scores over R(q); ties (s_max == T) are kept.
 
+A second gate, for comparison (``gate_mode="gap"``): the running-maximum
+reference that the pages attribute to BLASST and to SpargeAttention's
+in-kernel P.V skip (Sec. 3 "Related Work": gating on the gap to a running
+maximum rather than on a stored threshold).  The pages give no formula; the
+reading used here: key blocks are visited in increasing order (App. B.2) and
+off-diagonal tile j is skipped iff s_max(i, j) < M - tau, where M is the
+largest s_max among the tiles kept before j (-inf before the first) and tau
+is the table entry of (head, query block), read as the gap.
+
 Threshold calibration (Sec. 4.2, App. B.3): for each query block, sort the
 off-diagonal computed tiles by their maxima and put the threshold so exactly
 the top k are retained - here the midpoint between the k-th and (k+1)-th
@@ -57,6 +66,7 @@ __all__ = [
     "block_tile_maxima",
     "threshold_for",
     "gate",
+    "gate_gap",
     "masked_softmax_attention",
     "run_blocks",
     "run",
@@ -125,6 +135,26 @@ def gate(tile_max_row: np.ndarray, i: int, tau: float) -> np.ndarray:
     return skip
 
 
+def gate_gap(tile_max_row: np.ndarray, i: int, tau: float) -> np.ndarray:
+    """Skip decisions of the gap gate for query block i (see the module notes).
+
+    Tiles are visited in increasing key-block order; off-diagonal tile j is
+    skipped iff s_max(i, j) < M - tau with M the largest s_max of the tiles
+    kept so far.  IEEE arithmetic throughout: -inf - (-inf) is NaN, and a NaN
+    comparison keeps the tile.
+    """
+    n = tile_max_row.shape[0]
+    skip = np.zeros(n, dtype=bool)
+    m = -np.inf
+    with np.errstate(invalid="ignore"):
+        for j in range(n):
+            if j != i and tile_max_row[j] < np.float64(m) - np.float64(tau):
+                skip[j] = True
+            else:
+                m = max(m, float(tile_max_row[j]))
+    return skip
+
+
 def masked_softmax_attention(s: np.ndarray, keep: np.ndarray, v_rows: np.ndarray):
     """lse and output of softmax restricted to ``keep`` (App. B.2 + Sec. 4.4).
 
@@ -152,12 +182,14 @@ def run_blocks(
     block: int,
     blocks: Iterable[Tuple[int, int, int]],
     skip_override: Optional[np.ndarray] = None,
+    gate_mode: str = "threshold",
 ) -> List[dict]:
     """Evaluate selected query blocks ``(b, h, i)``.
 
     q: [B, H_q, N, d], k/v: [B, H_kv, N, d] (bf16 bits or floats);
     thresholds: [H_q, T_len].  ``skip_override`` ([B, H_q, M, M] bool) replaces
     the gate's decisions when given (diagonal tiles must stay kept).
+    ``gate_mode``: "threshold" (the pages' gate) or "gap" (``gate_gap``).
 
     Each result holds ``out`` [block, d], ``lse`` [block], ``tile_max`` [M]
     (NaN where not computed), ``tile_state`` [M] uint8 and ``skip_count``.
@@ -166,6 +198,8 @@ def run_blocks(
     Hkv = k.shape[1]
     if Hq % Hkv:
         raise ValueError("H_q must be a multiple of H_kv")
+    if gate_mode not in ("threshold", "gap"):
+        raise ValueError("gate_mode must be 'threshold' or 'gap'")
     G = Hq // Hkv
     M = N // block
     results = []
@@ -187,6 +221,8 @@ def run_blocks(
             skip = np.array(skip_override[b, h, i, : tmax.shape[0]], dtype=bool)
             if skip[i]:
                 raise ValueError("a diagonal tile cannot be skipped")
+        elif gate_mode == "gap":
+            skip = gate_gap(tmax, i, tau)
         else:
             skip = gate(tmax, i, tau)
         keep = vis & ~np.repeat(skip, block)[None, :]
@@ -212,7 +248,7 @@ def run_blocks(
     return results
 
 
-def run(q, k, v, thresholds, causal: bool, block: int, skip_override=None) -> dict:
+def run(q, k, v, thresholds, causal: bool, block: int, skip_override=None, gate_mode: str = "threshold") -> dict:
     """Whole-layer oracle: out [B,H_q,N,d], lse [B,H_q,N], skip_counts [B,H_q,M],
     tile_state [B,H_q,M,M] (uint8), tile_max [B,H_q,M,M] (NaN where not computed)."""
     B, Hq, N, d = q.shape
@@ -223,7 +259,7 @@ def run(q, k, v, thresholds, causal: bool, block: int, skip_override=None) -> di
     tile_state = np.empty((B, Hq, M, M), dtype=np.uint8)
     tile_max = np.empty((B, Hq, M, M))
     blocks = [(b, h, i) for b in range(B) for h in range(Hq) for i in range(M)]
-    for r in run_blocks(q, k, v, thresholds, causal, block, blocks, skip_override):
+    for r in run_blocks(q, k, v, thresholds, causal, block, blocks, skip_override, gate_mode):
         b, h, i = r["b"], r["h"], r["i"]
         rows = slice(i * block, (i + 1) * block)
         out[b, h, rows] = r["out"]

@@ -16,8 +16,12 @@ the pages claim, so this is an independent check.  Tiny inputs only.
 import math
 
 
-def brute_stream(q, k, v, thresholds, causal, block):
+def brute_stream(q, k, v, thresholds, causal, block, gate="threshold"):
     """q: [B][Hq][N][d] nested float lists (or arrays of Python floats).
+
+    ``gate="gap"``: the running-maximum gate instead of the stored threshold -
+    skip an off-diagonal tile whose maximum is below (largest maximum of the
+    tiles kept so far) minus the table entry.
 
     Returns (out, lse, skip_counts, tile_max) as nested lists; tile_max holds
     the maximum visible score of each computed tile (None where not computed).
@@ -45,6 +49,7 @@ def brute_stream(q, k, v, thresholds, causal, block):
                 l_run = [0.0] * block
                 acc = [[0.0] * d for _ in range(block)]
                 last = i if causal else M - 1
+                kept_max = -math.inf
                 for j in range(last + 1):
                     cols = list(range(j * block, (j + 1) * block))
                     s = [[None] * block for _ in range(block)]
@@ -62,9 +67,14 @@ def brute_stream(q, k, v, thresholds, causal, block):
                             if s[a][c] > tile_max:
                                 tile_max = s[a][c]
                     tmax[b][h][i][j] = tile_max
-                    if j != i and tile_max < tau:
+                    if gate == "gap":
+                        ref = math.nan if kept_max == -math.inf and tau == -math.inf else kept_max - tau
+                    else:
+                        ref = tau
+                    if j != i and tile_max < ref:
                         skips[b][h][i] += 1
                         continue
+                    kept_max = max(kept_max, tile_max)
                     for a in range(block):
                         vals = [(c, s[a][c]) for c in range(block) if s[a][c] is not None]
                         if not vals:

@@ -61,6 +61,40 @@ def margin_thresholds(tile_max: np.ndarray, k, causal: bool, margin: float = 2e-
     return out
 
 
+def gap_thresholds(tile_max: np.ndarray, causal: bool, base: float, margin: float = 2e-3,
+                   step: float = 0.037) -> np.ndarray:
+    """Gaps [H, M] (float32) for the gap gate, starting at ``base``, moved per
+    (head, query block) until no off-diagonal tile of any batch element lies
+    within ``margin`` of its decision boundary M - gap (float64, the oracle's
+    visiting order), so that the masks of the two sides must agree exactly."""
+    B, H, M, _ = tile_max.shape
+    out = np.empty((H, M), dtype=np.float32)
+    for h in range(H):
+        for i in range(M):
+            n = (i + 1) if causal else M
+            for t in range(200):
+                gap = np.float32(base + step * ((t + 1) // 2) * (1 if t % 2 else -1))
+                ok = True
+                for b in range(B):
+                    row = tile_max[b, h, i, :n]
+                    m = -np.inf
+                    for j in range(n):
+                        ref = m - float(gap)
+                        if j != i and np.isfinite(ref) and abs(row[j] - ref) <= margin:
+                            ok = False
+                            break
+                        if j == i or not row[j] < ref:
+                            m = max(m, row[j])
+                    if not ok:
+                        break
+                if ok:
+                    break
+            else:
+                raise RuntimeError("no gap with the required margin")
+            out[h, i] = gap
+    return out
+
+
 def exempt_tiles(oracle_tile_max: np.ndarray, thresholds: np.ndarray) -> np.ndarray:
     """[B, H, M, M] bool: off-diagonal computed tiles whose s_max is within EXEMPT of tau."""
     B, H, M, _ = oracle_tile_max.shape
@@ -72,9 +106,12 @@ def exempt_tiles(oracle_tile_max: np.ndarray, thresholds: np.ndarray) -> np.ndar
     return near
 
 
-def compare_blocks(gpu: dict, ref_blocks, block: int, thresholds: np.ndarray, label: str = ""):
+def compare_blocks(gpu: dict, ref_blocks, block: int, thresholds: np.ndarray, label: str = "",
+                   exempt: bool = True):
     """Compare GPU outputs (numpy, full arrays) with oracle ``run_blocks`` results.
 
+    ``exempt=False``: no tile is exempt from the mask comparison (inputs built
+    with a margin around every decision boundary, e.g. ``gap_thresholds``).
     Returns a dict of statistics.  Raises AssertionError on any violation.
     """
     errs = []
@@ -95,6 +132,8 @@ def compare_blocks(gpu: dict, ref_blocks, block: int, thresholds: np.ndarray, la
             near = np.zeros_like(computed)
             near[computed] = np.abs(r["tile_max"][computed] - tau) <= EXEMPT
             near[i] = False
+            if not exempt:
+                near[:] = False
             n_exempt += int(near.sum())
             bad = (st_gpu != st_ref) & ~near
             if bad.any():

@@ -88,3 +88,33 @@ def test_null_and_misaligned_pointers_rejected_before_any_launch(lib):
     assert f(None, None, None, None, None, None, None, S(N=1000), 1, blk, None) == 2
     assert lib.bsfa_prefill_ex(good, good, good, good, None, None, good, shape, 1, blk, None, good + 1,
                                None) == 4
+
+
+def test_bf16_and_gated_entry_points_reject_before_any_launch(lib):
+    shape, blk = S(), bb.make_block(128)
+    good = 0x100000
+    f = lib.bsfa_prefill_bf16
+    assert f(good, good, good, None, None, None, good, shape, 1, blk, None) == 1  # no output
+    assert f(good, good, good, good + 8, None, None, good, shape, 1, blk, None) == 4  # bf16 out not 16-B aligned
+    assert f(None, None, None, None, None, None, None, S(N=1000), 1, blk, None) == 2
+    g = lib.bsfa_prefill_gated
+    for bad_gate in (-1, 2, 7):  # unknown gate: shape status, before the pointer checks
+        assert g(good, good, good, good, None, None, good, shape, 1, blk, bad_gate, None, None, None) == 2
+    assert g(good, good, good, None, None, None, good, shape, 1, blk, bb.GATE_GAP, None, None, None) == 1
+    assert g(good, good, good, good, None, None, good, shape, 1, blk, bb.GATE_GAP, None, good + 2, None) == 4
+
+
+def test_calibrate_levels_rejects_before_any_launch(lib):
+    import ctypes
+
+    good = 0x100000
+    ks = (ctypes.c_int64 * 3)(2, 5, 9)
+    f = lib.bsfa_calibrate_levels
+    pks = ctypes.cast(ks, ctypes.c_void_p)
+    assert f(good, 1, 4, 8, 1, None, 3, good, None) == 1        # ks missing
+    assert f(good, 1, 4, 8, 1, pks, 0, good, None) == 2         # no level
+    bad = (ctypes.c_int64 * 2)(3, -1)
+    assert f(good, 1, 4, 8, 1, ctypes.cast(bad, ctypes.c_void_p), 2, good, None) == 2  # negative k
+    assert f(good, 1, 4, 20000, 1, pks, 3, good, None) == 3     # M beyond the calibration kernel
+    assert f(good + 2, 1, 4, 8, 1, pks, 3, good, None) == 4     # misaligned tile maxima
+    assert f(good, 1, 4, 8, 2, pks, 3, good, None) == 2         # causal flag

@@ -11,6 +11,7 @@ import pytest
 
 import oracle
 from oracle import bsfa_oracle as ob
+import test_oracle_gap_gate as gap_pins
 import test_oracle_pins as pins
 
 
@@ -40,17 +41,36 @@ def _mut_tile_max_all(s, vis, block):  # maximum over masked entries too
 _ORIG_RUN_BLOCKS = ob.run_blocks
 
 
-def _mut_gqa_modulo(q, k, v, thresholds, causal, block, blocks, skip_override=None):
+def _mut_gqa_modulo(q, k, v, thresholds, causal, block, blocks, skip_override=None, gate_mode="threshold"):
     # KV head h % H_kv instead of the contiguous h // G: permute q heads so the
     # real routine sees the interleaved grouping
     Hq, Hkv = q.shape[1], k.shape[1]
     G = Hq // Hkv
     perm = np.array([(h % Hkv) * G + h // Hkv for h in range(Hq)])
     res = _ORIG_RUN_BLOCKS(q[:, perm], k, v, thresholds[perm], causal, block,
-                           [(b, int(np.flatnonzero(perm == h)[0]), i) for b, h, i in blocks], skip_override)
+                           [(b, int(np.flatnonzero(perm == h)[0]), i) for b, h, i in blocks], skip_override,
+                           gate_mode)
     for r, (b, h, i) in zip(res, blocks):
         r["h"] = h
     return res
+
+
+def _mut_gap_global_max(tile_max_row, i, tau):  # reference = max over every tile, not the running max
+    skip = tile_max_row < np.max(tile_max_row) - tau
+    skip[i] = False
+    return skip
+
+
+def _mut_gap_sign(tile_max_row, i, tau):  # M + tau instead of M - tau
+    n = tile_max_row.shape[0]
+    skip = np.zeros(n, dtype=bool)
+    m = -np.inf
+    for j in range(n):
+        if j != i and tile_max_row[j] < m + tau:
+            skip[j] = True
+        else:
+            m = max(m, float(tile_max_row[j]))
+    return skip
 
 
 MUTANTS = [
@@ -61,6 +81,9 @@ MUTANTS = [
     ("block_tile_maxima", _mut_tile_max_all,
      lambda: pins.test_oracle_matches_brute_force_streaming(True, 1, 2, 1, 256, 16, 4, 3)),
     ("run_blocks", _mut_gqa_modulo, lambda: pins.test_dense_threshold_equals_library_attention(False)),
+    ("gate_gap", _mut_gap_global_max,
+     lambda: gap_pins.test_gap_gate_matches_brute_force_streaming(True, 1, 2, 1, 256, 16, 4, 21)),
+    ("gate_gap", _mut_gap_sign, lambda: gap_pins.test_uniform_scores_closed_form(True)),
 ]
 
 
