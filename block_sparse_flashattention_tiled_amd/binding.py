@@ -144,7 +144,7 @@ def _check_all(q, k, v, out, lse, skip_counts, thresholds, shape, block, tile_st
         raise ValueError("tensors must live on the GPU")
     B, Hq, Hkv, N, d, T = (shape.batch, shape.n_heads_q, shape.n_heads_kv, shape.seq_len, shape.head_dim,
                            shape.thr_len)
-    M = N // block.bm if block.bm > 0 else 0
+    M = -(-N // block.bm) if block.bm > 0 else 0
     _check(q, "q", torch.bfloat16, (B, Hq, N, d), dev)
     _check(k, "k", torch.bfloat16, (B, Hkv, N, d), dev)
     _check(v, "v", torch.bfloat16, (B, Hkv, N, d), dev)
@@ -235,7 +235,7 @@ def bsfa_tile_max(q, k, tile_max, shape: BsfaShape, causal: int, block: BsfaBloc
         raise BsfaError(st, "bsfa_tile_max")
     dev = q.device
     B, Hq, Hkv, N, d = shape.batch, shape.n_heads_q, shape.n_heads_kv, shape.seq_len, shape.head_dim
-    M = N // block.bm
+    M = -(-N // block.bm)
     _check(q, "q", torch.bfloat16, (B, Hq, N, d), dev)
     _check(k, "k", torch.bfloat16, (B, Hkv, N, d), dev)
     _check(tile_max, "tile_max", torch.float32, (B, Hq, M, M), dev)
@@ -260,7 +260,7 @@ def tile_max(q: torch.Tensor, k: torch.Tensor, causal: bool, block: int, stream=
     """Allocate and fill the [B, H_q, M, M] tile maxima (``bsfa_tile_max``)."""
     B, Hq, N, d = q.shape
     shape = make_shape(B, Hq, k.shape[1], N, d, 1)
-    M = N // block
+    M = -(-N // block)  # the last block may be partial
     out = torch.empty((B, Hq, M, M), dtype=torch.float32, device=q.device)
     bsfa_tile_max(q, k, out, shape, int(causal), make_block(block), stream)
     return out
@@ -299,7 +299,7 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, thresholds: torch
     Hkv = k.shape[1]
     shape = make_shape(B, Hq, Hkv, N, d, thresholds.shape[1])
     blk = make_block(block)
-    M = N // block
+    M = -(-N // block)  # the last block may be partial
     dev = q.device
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("out_dtype must be float32 or bfloat16")

@@ -21,10 +21,9 @@ int check_shape(const bsfa_shape& s, int causal, const bsfa_block& blk) {
   if (blk.bm != blk.bn) return BSFA_ERR_UNSUPPORTED;
   if (blk.bm != 64 && blk.bm != 128) return BSFA_ERR_UNSUPPORTED;
   if (s.head_dim != 64 && s.head_dim != 128) return BSFA_ERR_UNSUPPORTED;
-  if (s.seq_len % blk.bm) return BSFA_ERR_SHAPE;
   // the kernels index heads, rows and thresholds with 32-bit integers
   const int64_t lim = INT32_MAX;
-  const int64_t m = s.seq_len / blk.bm;
+  const int64_t m = (s.seq_len + blk.bm - 1) / blk.bm;  // the last block may be partial
   if (s.seq_len > lim / 2 || s.batch > lim || s.n_heads_q > lim) return BSFA_ERR_SHAPE;
   if (s.batch * s.n_heads_q > lim / m) return BSFA_ERR_SHAPE;    // workgroups
   if (s.n_heads_q > lim / s.thr_len) return BSFA_ERR_SHAPE;      // threshold index
@@ -39,7 +38,7 @@ bsfa::FwdParams shape_params(const bsfa_shape& shape, const bsfa_block& block) {
   p.Hkv = (int)shape.n_heads_kv;
   p.G = p.Hq / p.Hkv;
   p.N = (int)shape.seq_len;
-  p.M = (int)(shape.seq_len / block.bm);
+  p.M = (int)((shape.seq_len + block.bm - 1) / block.bm);
   p.T_len = (int)shape.thr_len;
   p.scale = (float)(1.0 / sqrt((double)shape.head_dim));
   p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)shape.head_dim));

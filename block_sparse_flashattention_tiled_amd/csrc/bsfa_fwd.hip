@@ -137,6 +137,29 @@ __device__ __forceinline__ void store_out_row(const FwdParams& p, size_t row, co
     }
 }
 
+// Sequences whose length N is not a multiple of the tile: the last query and
+// key blocks are partial, and positions >= N do not exist (masked, not padded).
+// tile_chunk: index of 16-byte chunk c of the tile whose first row is r0, with
+// rows past the end reading the last row instead, so that every load stays
+// inside the tensor; mask_tail sets the scores of query rows >= rows_left and of
+// keys >= keys_left (both relative to the tile) to -inf, so the values read
+// there never reach a maximum, a sum or an output.
+template <int CPR>
+__device__ __forceinline__ size_t tile_chunk(int r0, int c, int n) {
+  const int row = min(r0 + c / CPR, n - 1);
+  return (size_t)row * CPR + c % CPR;
+}
+template <int NKB>
+__device__ __forceinline__ void mask_tail(f32x16 (&s)[NKB], int qloc, int hh, int rows_left, int keys_left) {
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      if (qloc >= rows_left || key >= keys_left) s[kb][r] = -INFINITY;
+    }
+}
+
 // S^T = K_j Q_i^T for this wave's 32 query rows.
 // s[kb][r] = raw score of query row (lane % 32) and key kb*32 + 8(r/4) + 4(lane/32) + r%4.
 template <int D, int BLK, int NKB, int NKC>
@@ -160,7 +183,7 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[NKB], const char* ks, int k_
 
 // MAXONLY: calibration pass - only the tile maxima of every computed tile are
 // produced (no gate, no V, no output); used to build threshold tables.
-template <int D, int BLK, bool CAUSAL, bool DIAG_OUT, bool MAXONLY>
+template <int D, int BLK, bool CAUSAL, bool DIAG_OUT, bool MAXONLY, bool RAGGED>
 __global__ void __launch_bounds__(BLK * 2) bsfa_fwd_kernel(const FwdParams p) {
   using C = Cfg<D, BLK>;
   __shared__ __attribute__((aligned(16))) char v_lds[C::V_BYTES];
@@ -210,7 +233,7 @@ __global__ void __launch_bounds__(BLK * 2) bsfa_fwd_kernel(const FwdParams p) {
   // ---- (a2) Q_i stays in registers: B operand of S^T = K Q^T --------------
   bf16x8 qf[C::KC];
   {
-    const u32x4* qg = reinterpret_cast<const u32x4*>(p.q) + (q_head + qrow) * C::CPR;
+    const u32x4* qg = reinterpret_cast<const u32x4*>(p.q) + (q_head + (RAGGED ? min(qrow, p.N - 1) : qrow)) * C::CPR;
 #pragma unroll
     for (int c = 0; c < C::KC; ++c) qf[c] = __builtin_bit_cast(bf16x8, qg[2 * c + hh]);
   }
@@ -235,7 +258,10 @@ __global__ void __launch_bounds__(BLK * 2) bsfa_fwd_kernel(const FwdParams p) {
   u32x4 kreg[C::LD];
   u32x4 vreg[C::LD];
 #pragma unroll
-  for (int it = 0; it < C::LD; ++it) kreg[it] = kg[tid + C::NT * it];
+  for (int it = 0; it < C::LD; ++it) {
+    const int c = tid + C::NT * it;
+    kreg[it] = kg[RAGGED ? tile_chunk<C::CPR>(0, c, p.N) : c];
+  }
 #pragma unroll
   for (int it = 0; it < C::LD; ++it) {
     const int c = tid + C::NT * it;
@@ -249,7 +275,10 @@ __global__ void __launch_bounds__(BLK * 2) bsfa_fwd_kernel(const FwdParams p) {
     if (more) {
       const u32x4* src = kg + (size_t)(j + 1) * TILE_CHUNKS;
 #pragma unroll
-      for (int it = 0; it < C::LD; ++it) kreg[it] = src[tid + C::NT * it];
+      for (int it = 0; it < C::LD; ++it) {
+        const int c = tid + C::NT * it;
+        kreg[it] = RAGGED ? kg[tile_chunk<C::CPR>((j + 1) * BLK, c, p.N)] : src[c];
+      }
     }
     // ---- (a4) S^T = K_j Q_i^T on MFMA --------------------------------------
     f32x16 s[C::KB];
@@ -263,6 +292,10 @@ __global__ void __launch_bounds__(BLK * 2) bsfa_fwd_kernel(const FwdParams p) {
           const int key = kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
           if (key > qloc) s[kb][r] = -INFINITY;
         }
+    }
+    if (RAGGED) {
+      const int rows_left = p.N - i * BLK, keys_left = p.N - j * BLK;
+      if (rows_left < BLK || keys_left < BLK) mask_tail(s, qloc, hh, rows_left, keys_left);
     }
     // ---- (a5) tile maximum and gate ---------------------------------------
     float rm0 = -INFINITY, rm1 = -INFINITY;
@@ -294,7 +327,10 @@ __global__ void __launch_bounds__(BLK * 2) bsfa_fwd_kernel(const FwdParams p) {
     if (!skip) {
       const u32x4* src = vg + (size_t)j * TILE_CHUNKS;
 #pragma unroll
-      for (int it = 0; it < C::LD; ++it) vreg[it] = src[tid + C::NT * it];
+      for (int it = 0; it < C::LD; ++it) {
+        const int c = tid + C::NT * it;
+        vreg[it] = RAGGED ? vg[tile_chunk<C::CPR>(j * BLK, c, p.N)] : src[c];
+      }
     }
     // K_{j+1} -> LDS (every wave has finished reading K_j)
     if (more) {
@@ -380,8 +416,10 @@ __global__ void __launch_bounds__(BLK * 2) bsfa_fwd_kernel(const FwdParams p) {
   // ---- (a9) epilogue: O_i = O_acc / l, lse, skip count -------------------
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.f / (lb_run + __shfl_xor(lb_run, 32));
-  store_out_row(p, q_head + qrow, o, inv, hh);
-  if (p.lse && hh == 0) p.lse[q_head + qrow] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
+  if (!RAGGED || qrow < p.N) {
+    store_out_row(p, q_head + qrow, o, inv, hh);
+    if (p.lse && hh == 0) p.lse[q_head + qrow] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
+  }
   if (p.skip_counts && tid == 0) p.skip_counts[(size_t)(b * p.Hq + hq) * p.M + i] = nskip;
   if (DIAG_OUT && CAUSAL) {
     for (int jj = i + 1 + tid; jj < p.M; jj += C::NT) {
@@ -432,7 +470,7 @@ __device__ __forceinline__ void qk_tile_qlds(f32x16 (&s)[NKB], const char* ks, i
 
 // HEADPAIR: units are query heads 2hp, 2hp+1 of a KV group (same query block);
 // otherwise (bidirectional only) query blocks 2ip, 2ip+1 of one head.
-template <int D, int BLK, bool CAUSAL, bool DIAG_OUT, bool MAXONLY, bool HEADPAIR>
+template <int D, int BLK, bool CAUSAL, bool DIAG_OUT, bool MAXONLY, bool HEADPAIR, bool RAGGED>
 __global__ void __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2, 2)))
     bsfa_fwd_pair_kernel(const FwdParams p) {
   using C = Cfg<D, BLK>;
@@ -493,11 +531,14 @@ __global__ void __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2,
   // ---- (a2) Q of both units -> LDS ------------------------------------------
 #pragma unroll
   for (int uu = 0; uu < 2; ++uu) {
-    const u32x4* qg = reinterpret_cast<const u32x4*>(p.q) +
-                      ((size_t)(b * p.Hq + hq_u[uu]) * p.N + (size_t)i_u[uu] * BLK) * C::CPR;
+    const u32x4* qh = reinterpret_cast<const u32x4*>(p.q) + (size_t)(b * p.Hq + hq_u[uu]) * p.N * C::CPR;
+    const u32x4* qg = qh + (size_t)i_u[uu] * BLK * C::CPR;
     u32x4 qr[P2::LD];
 #pragma unroll
-    for (int it = 0; it < P2::LD; ++it) qr[it] = qg[tid + P2::NT * it];
+    for (int it = 0; it < P2::LD; ++it) {
+      const int c = tid + P2::NT * it;
+      qr[it] = RAGGED ? qh[tile_chunk<C::CPR>(i_u[uu] * BLK, c, p.N)] : qg[c];
+    }
 #pragma unroll
     for (int it = 0; it < P2::LD; ++it) {
       const int c = tid + P2::NT * it;
@@ -527,7 +568,10 @@ __global__ void __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2,
   u32x4 kreg[P2::LD];
   u32x4 vreg[P2::LD];
 #pragma unroll
-  for (int it = 0; it < P2::LD; ++it) kreg[it] = kg[tid + P2::NT * it];
+  for (int it = 0; it < P2::LD; ++it) {
+    const int c = tid + P2::NT * it;
+    kreg[it] = kg[RAGGED ? tile_chunk<C::CPR>(0, c, p.N) : c];
+  }
 #pragma unroll
   for (int it = 0; it < P2::LD; ++it) {
     const int c = tid + P2::NT * it;
@@ -544,7 +588,10 @@ __global__ void __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2,
     if (more) {
       const u32x4* src = kg + (size_t)(j + 1) * TILE_CHUNKS;
 #pragma unroll
-      for (int it = 0; it < P2::LD; ++it) kreg[it] = src[tid + P2::NT * it];
+      for (int it = 0; it < P2::LD; ++it) {
+        const int c = tid + P2::NT * it;
+        kreg[it] = RAGGED ? kg[tile_chunk<C::CPR>((j + 1) * BLK, c, p.N)] : src[c];
+      }
     }
     // ---- (a4) S^T = K_j Q^T ------------------------------------------------
     f32x16 s[C::KB];
@@ -557,6 +604,10 @@ __global__ void __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2,
           const int key = kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
           if (key > qloc) s[kb][r] = -INFINITY;
         }
+    }
+    if constexpr (RAGGED) {
+      const int rows_left = p.N - i * BLK, keys_left = p.N - j * BLK;
+      if (rows_left < BLK || keys_left < BLK) mask_tail(s, qloc, hh, rows_left, keys_left);
     }
     // ---- (a5) tile maxima of both units and their gates ---------------------
     float rm0 = -INFINITY, rm1 = -INFINITY;
@@ -593,7 +644,10 @@ __global__ void __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2,
     if (need_v) {
       const u32x4* src = vg + (size_t)j * TILE_CHUNKS;
 #pragma unroll
-      for (int it = 0; it < P2::LD; ++it) vreg[it] = src[tid + P2::NT * it];
+      for (int it = 0; it < P2::LD; ++it) {
+        const int c = tid + P2::NT * it;
+        vreg[it] = RAGGED ? vg[tile_chunk<C::CPR>(j * BLK, c, p.N)] : src[c];
+      }
     }
     if (more) {
 #pragma unroll
@@ -681,8 +735,10 @@ __global__ void __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2,
   // ---- (a9) epilogue -------------------------------------------------------
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.f / (lb_run + __shfl_xor(lb_run, 32));
-  store_out_row(p, q_head + qrow, o, inv, hh);
-  if (p.lse && hh == 0) p.lse[q_head + qrow] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
+  if (!RAGGED || qrow < p.N) {
+    store_out_row(p, q_head + qrow, o, inv, hh);
+    if (p.lse && hh == 0) p.lse[q_head + qrow] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
+  }
   if (p.skip_counts && utid == 0) p.skip_counts[(size_t)(b * p.Hq + hq) * p.M + i] = nskip;
   if (DIAG_OUT && CAUSAL) {
     for (int jj = i + 1 + utid; jj < p.M; jj += UNT) {
@@ -692,34 +748,42 @@ __global__ void __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2,
   }
 }
 
-template <int D, int BLK, bool CAUSAL, bool DIAG_OUT, bool MAXONLY>
+template <int D, int BLK, bool CAUSAL, bool DIAG_OUT, bool MAXONLY, bool RAGGED>
 static int launch_one(const FwdParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((size_t)p.B * p.Hq * p.M));
   const dim3 block(BLK * 2);
-  hipLaunchKernelGGL((bsfa_fwd_kernel<D, BLK, CAUSAL, DIAG_OUT, MAXONLY>), grid, block, 0, stream, p);
+  hipLaunchKernelGGL((bsfa_fwd_kernel<D, BLK, CAUSAL, DIAG_OUT, MAXONLY, RAGGED>), grid, block, 0, stream, p);
   return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 
-template <int D, int BLK, bool CAUSAL, bool DIAG_OUT, bool MAXONLY, bool HEADPAIR>
+template <int D, int BLK, bool CAUSAL, bool DIAG_OUT, bool MAXONLY, bool HEADPAIR, bool RAGGED>
 static int launch_pair(FwdParams p, hipStream_t stream) {
   const size_t units = (size_t)p.B * p.Hq * p.M;
   const int per_group = HEADPAIR ? p.G / 2 : p.G;
   p.remap = ((units / 2) % (8 * (size_t)per_group) == 0) ? 1 : 0;
   const dim3 grid((unsigned)(units / 2));
   const dim3 block(BLK * 4);
-  hipLaunchKernelGGL((bsfa_fwd_pair_kernel<D, BLK, CAUSAL, DIAG_OUT, MAXONLY, HEADPAIR>), grid, block, 0, stream,
-                     p);
+  hipLaunchKernelGGL((bsfa_fwd_pair_kernel<D, BLK, CAUSAL, DIAG_OUT, MAXONLY, HEADPAIR, RAGGED>), grid, block, 0,
+                     stream, p);
   return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 
 // Two units per workgroup when they can share one K/V stream: query-head
 // pairs when the GQA group size is even, neighbouring query blocks of one head
 // when attention is bidirectional; otherwise one unit per workgroup.
+template <int D, int BLK, bool CAUSAL, bool DIAG_OUT, bool MAXONLY, bool RAGGED>
+static int launch_units_r(const FwdParams& p, hipStream_t s) {
+  if (p.G % 2 == 0) return launch_pair<D, BLK, CAUSAL, DIAG_OUT, MAXONLY, true, RAGGED>(p, s);
+  if (!CAUSAL && p.M % 2 == 0) return launch_pair<D, BLK, false, DIAG_OUT, MAXONLY, false, RAGGED>(p, s);
+  return launch_one<D, BLK, CAUSAL, DIAG_OUT, MAXONLY, RAGGED>(p, s);
+}
+
+// A sequence length that is not a multiple of the tile selects the kernels
+// compiled with the tail handling; aligned lengths run without it.
 template <int D, int BLK, bool CAUSAL, bool DIAG_OUT, bool MAXONLY>
 static int launch_units(const FwdParams& p, hipStream_t s) {
-  if (p.G % 2 == 0) return launch_pair<D, BLK, CAUSAL, DIAG_OUT, MAXONLY, true>(p, s);
-  if (!CAUSAL && p.M % 2 == 0) return launch_pair<D, BLK, false, DIAG_OUT, MAXONLY, false>(p, s);
-  return launch_one<D, BLK, CAUSAL, DIAG_OUT, MAXONLY>(p, s);
+  if (p.N % BLK) return launch_units_r<D, BLK, CAUSAL, DIAG_OUT, MAXONLY, true>(p, s);
+  return launch_units_r<D, BLK, CAUSAL, DIAG_OUT, MAXONLY, false>(p, s);
 }
 
 // mode: 0 = forward, 1 = forward with per-tile diagnostics, 2 = tile maxima only

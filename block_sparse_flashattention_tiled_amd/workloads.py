@@ -76,7 +76,7 @@ class Workload:
 
     @property
     def n_blocks(self) -> int:
-        return self.seq_len // self.block
+        return -(-self.seq_len // self.block)  # the last block may be partial
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -239,8 +239,6 @@ def generate(w: Workload, seed: int = 0) -> dict:
     ``[B, H, N, d]`` (C order) plus ``"planted"``: a list of
     ``(b, h_q, q_pos, k_pos)`` for every planted key.
     """
-    if w.seq_len % w.block:
-        raise ValueError("sequence length must be a multiple of the block size")
     if w.kind == "tiny":
         q, k, v, planted = _gen_tiny(w, seed)
     elif w.kind == "llama":

@@ -41,9 +41,14 @@ typedef struct {
   int64_t batch;      /* B    >= 1 */
   int64_t n_heads_q;  /* H_q  >= 1 */
   int64_t n_heads_kv; /* H_kv >= 1, H_q % H_kv == 0 */
-  int64_t seq_len;    /* N    >= 1 and a multiple of the block size.  The pages
-                         pad a non-aligned sequence by repeating its last token
-                         (App. B.3); that padding is the caller's. */
+  int64_t seq_len;    /* N    >= 1.  M = ceil(N / bm) query blocks and key blocks;
+                         when N is not a multiple of bm the last block of each
+                         is partial and positions >= N do not exist: they are
+                         neither keys nor queries, take no part in any tile
+                         maximum, and their output rows are not written.  (The
+                         pages instead pad to a multiple of the tile by
+                         repeating the last token, App. B.3; a caller who wants
+                         that result pads before the call.) */
   int64_t head_dim;   /* d in {64, 128} */
   int64_t thr_len;    /* T_len >= 1: thresholds per head.  Query block i uses
                          entry min(i, T_len - 1): blocks past the table reuse
@@ -97,7 +102,7 @@ enum {
  *                    S = Q K^T / sqrt(d) (Sec. 2) and R(q) the visible keys
  *                    of the kept tiles of q's query block
  *  lse         fp32  [B, H_q, N] natural-log sum of exp(S) over R(q); NULL = not written
- *  skip_counts int32 [B, H_q, N / bm] number of skipped tiles per query block;
+ *  skip_counts int32 [B, H_q, M] number of skipped tiles per query block;
  *                    NULL = not written
  *  thresholds  fp32  [H_q, T_len] in the scaled-score domain (the same units
  *                    as S).  Tile (i, j), j != i, is skipped iff
@@ -114,7 +119,7 @@ int bsfa_prefill(const void* q, const void* k, const void* v, float* out, float*
 
 /*
  * bsfa_prefill_ex - bsfa_prefill plus per-tile diagnostics (each nullable):
- *  tile_state uint8 [B, H_q, M, M] (M = N / bm): BSFA_TILE_* of every tile
+ *  tile_state uint8 [B, H_q, M, M] (M = ceil(N / bm)): BSFA_TILE_* of every tile
  *  tile_max   fp32  [B, H_q, M, M]: the gate's s_max (maximum scaled score over
  *             the visible entries) of every computed tile, NaN where not computed.
  * Same contract as bsfa_prefill otherwise.  Slower: for testing and

@@ -14,7 +14,10 @@ What is computed, per batch b and query head h (KV head g = h // G):
   "Scaled dot-product attention"; App. B.2 step (3)).
 * Queries are cut into blocks of ``block`` rows, keys into blocks of
   ``block`` columns; tile (i, j) pairs query block i with key block j
-  (App. B.2).  Under causal masking key k is visible to query q iff k <= q,
+  (App. B.2).  M = ceil(N / block): when N is not a multiple of the block the
+  last query block and the last key block are partial, and positions >= N do
+  not exist (a reading: the pages pad to a multiple by repeating the last
+  token, App. B.3, which makes the padding tokens keys of every query).  Under causal masking key k is visible to query q iff k <= q,
   and tiles with j > i hold no visible pair, so they are not computed
   (App. B.2, "approximately half for causal").
 * Each computed tile has a maximum score s_max(i, j), taken over its visible
@@ -99,21 +102,22 @@ def block_scores(q_rows: np.ndarray, k_cols: np.ndarray, head_dim: int) -> np.nd
     return (q_rows @ k_cols.T) / math.sqrt(head_dim)
 
 
-def _visible(i: int, block: int, n_keys: int, causal: bool) -> np.ndarray:
-    """Visibility of keys [0, n_keys) to the rows of query block i."""
-    qpos = np.arange(i * block, (i + 1) * block)[:, None]
+def _visible(q0: int, n_rows: int, n_keys: int, causal: bool) -> np.ndarray:
+    """Visibility of keys [0, n_keys) to query rows [q0, q0 + n_rows)."""
+    qpos = np.arange(q0, q0 + n_rows)[:, None]
     kpos = np.arange(n_keys)[None, :]
     if causal:
         return kpos <= qpos
-    return np.ones((block, n_keys), dtype=bool)
+    return np.ones((n_rows, n_keys), dtype=bool)
 
 
 def block_tile_maxima(s: np.ndarray, vis: np.ndarray, block: int) -> np.ndarray:
-    """s_max(i, j) over the visible entries of each computed key block j (Sec. 4.1)."""
-    n_tiles = s.shape[1] // block
+    """s_max(i, j) over the visible entries of each computed key block j (Sec. 4.1);
+    the last key block may be partial."""
+    n_tiles = -(-s.shape[1] // block)
     out = np.empty(n_tiles)
     for j in range(n_tiles):
-        cols = slice(j * block, (j + 1) * block)
+        cols = slice(j * block, min((j + 1) * block, s.shape[1]))
         out[j] = s[:, cols][vis[:, cols]].max()
     return out
 
@@ -201,7 +205,7 @@ def run_blocks(
     if gate_mode not in ("threshold", "gap"):
         raise ValueError("gate_mode must be 'threshold' or 'gap'")
     G = Hq // Hkv
-    M = N // block
+    M = -(-N // block)
     results = []
     cache = {}
     for b, h, i in blocks:
@@ -211,10 +215,11 @@ def run_blocks(
             cache.clear()
             cache[key] = (to_f64(k[b, g]), to_f64(v[b, g]))
         kf, vf = cache[key]
-        n_keys = (i + 1) * block if causal else N
-        q_rows = to_f64(q[b, h, i * block : (i + 1) * block])
+        r_end = min((i + 1) * block, N)
+        n_keys = r_end if causal else N
+        q_rows = to_f64(q[b, h, i * block : r_end])
         s = block_scores(q_rows, kf[:n_keys], d)
-        vis = _visible(i, block, n_keys, causal)
+        vis = _visible(i * block, r_end - i * block, n_keys, causal)
         tmax = block_tile_maxima(s, vis, block)
         tau = threshold_for(thresholds, h, i)
         if skip_override is not None:
@@ -225,7 +230,7 @@ def run_blocks(
             skip = gate_gap(tmax, i, tau)
         else:
             skip = gate(tmax, i, tau)
-        keep = vis & ~np.repeat(skip, block)[None, :]
+        keep = vis & ~np.repeat(skip, block)[None, :n_keys]
         out, lse = masked_softmax_attention(s, keep, vf[:n_keys])
         tile_max = np.full(M, np.nan)
         tile_max[: tmax.shape[0]] = tmax
@@ -252,7 +257,7 @@ def run(q, k, v, thresholds, causal: bool, block: int, skip_override=None, gate_
     """Whole-layer oracle: out [B,H_q,N,d], lse [B,H_q,N], skip_counts [B,H_q,M],
     tile_state [B,H_q,M,M] (uint8), tile_max [B,H_q,M,M] (NaN where not computed)."""
     B, Hq, N, d = q.shape
-    M = N // block
+    M = -(-N // block)
     out = np.empty((B, Hq, N, d))
     lse = np.empty((B, Hq, N))
     skip_counts = np.empty((B, Hq, M), dtype=np.int64)
@@ -261,7 +266,7 @@ def run(q, k, v, thresholds, causal: bool, block: int, skip_override=None, gate_
     blocks = [(b, h, i) for b in range(B) for h in range(Hq) for i in range(M)]
     for r in run_blocks(q, k, v, thresholds, causal, block, blocks, skip_override, gate_mode):
         b, h, i = r["b"], r["h"], r["i"]
-        rows = slice(i * block, (i + 1) * block)
+        rows = slice(i * block, min((i + 1) * block, N))
         out[b, h, rows] = r["out"]
         lse[b, h, rows] = r["lse"]
         skip_counts[b, h, i] = r["skip_count"]
@@ -285,7 +290,7 @@ def tile_maxima(q, k, causal: bool, block: int, heads: Optional[Sequence[int]] =
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
     G = Hq // Hkv
-    M = N // block
+    M = -(-N // block)
     out = np.full((B, Hq, M, M), np.nan)
     heads = range(Hq) if heads is None else heads
     rows = range(M) if rows is None else rows
@@ -293,9 +298,10 @@ def tile_maxima(q, k, causal: bool, block: int, heads: Optional[Sequence[int]] =
         for h in heads:
             kf = to_f64(k[b, h // G])
             for i in rows:
-                n_keys = (i + 1) * block if causal else N
-                s = block_scores(to_f64(q[b, h, i * block : (i + 1) * block]), kf[:n_keys], d)
-                tm = block_tile_maxima(s, _visible(i, block, n_keys, causal), block)
+                r_end = min((i + 1) * block, N)
+                n_keys = r_end if causal else N
+                s = block_scores(to_f64(q[b, h, i * block : r_end]), kf[:n_keys], d)
+                tm = block_tile_maxima(s, _visible(i * block, r_end - i * block, n_keys, causal), block)
                 out[b, h, i, : tm.shape[0]] = tm
     return out
 

@@ -32,7 +32,7 @@ def brute_stream(q, k, v, thresholds, causal, block, gate="threshold"):
     d = len(q[0][0][0])
     Hkv = len(k[0])
     G = Hq // Hkv
-    M = N // block
+    M = -(-N // block)  # the last block may be partial
     t_len = len(thresholds[0])
     inv = 1.0 / math.sqrt(d)
     out = [[[None] * N for _ in range(Hq)] for _ in range(B)]
@@ -44,15 +44,15 @@ def brute_stream(q, k, v, thresholds, causal, block, gate="threshold"):
             g = h // G
             for i in range(M):
                 tau = thresholds[h][min(i, t_len - 1)]
-                rows = list(range(i * block, (i + 1) * block))
-                m_run = [-math.inf] * block
-                l_run = [0.0] * block
-                acc = [[0.0] * d for _ in range(block)]
+                rows = list(range(i * block, min((i + 1) * block, N)))
+                m_run = [-math.inf] * len(rows)
+                l_run = [0.0] * len(rows)
+                acc = [[0.0] * d for _ in range(len(rows))]
                 last = i if causal else M - 1
                 kept_max = -math.inf
                 for j in range(last + 1):
-                    cols = list(range(j * block, (j + 1) * block))
-                    s = [[None] * block for _ in range(block)]
+                    cols = list(range(j * block, min((j + 1) * block, N)))
+                    s = [[None] * len(cols) for _ in range(len(rows))]
                     tile_max = -math.inf
                     for a, qr in enumerate(rows):
                         for c, kc in enumerate(cols):
@@ -75,8 +75,8 @@ def brute_stream(q, k, v, thresholds, causal, block, gate="threshold"):
                         skips[b][h][i] += 1
                         continue
                     kept_max = max(kept_max, tile_max)
-                    for a in range(block):
-                        vals = [(c, s[a][c]) for c in range(block) if s[a][c] is not None]
+                    for a in range(len(rows)):
+                        vals = [(c, s[a][c]) for c in range(len(cols)) if s[a][c] is not None]
                         if not vals:
                             continue
                         m_new = max(m_run[a], max(x for _, x in vals))

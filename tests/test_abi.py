@@ -49,7 +49,8 @@ def S(B=1, Hq=4, Hkv=2, N=1024, d=128, T=8):
     [
         (S(), 1, 128, 0),
         (S(d=64), 0, 64, 0),
-        (S(N=1000), 1, 128, 2),      # not a multiple of the tile
+        (S(N=1000), 1, 128, 0),      # not a multiple of the tile: the last block is partial
+        (S(N=1), 0, 64, 0),          # a single position
         (S(Hq=3, Hkv=2), 1, 128, 2),  # H_q % H_kv
         (S(d=96), 1, 128, 3),        # unsupported head dim
         (S(), 1, 96, 3),             # unsupported tile
@@ -85,7 +86,7 @@ def test_null_and_misaligned_pointers_rejected_before_any_launch(lib):
     assert f(good, good, good, good + 4, None, None, good, shape, 1, blk, None) == 4
     assert f(good, good, good, good, good + 2, None, good, shape, 1, blk, None) == 4
     # shape errors win over pointer errors
-    assert f(None, None, None, None, None, None, None, S(N=1000), 1, blk, None) == 2
+    assert f(None, None, None, None, None, None, None, S(Hq=3, Hkv=2), 1, blk, None) == 2
     assert lib.bsfa_prefill_ex(good, good, good, good, None, None, good, shape, 1, blk, None, good + 1,
                                None) == 4
 
@@ -96,7 +97,7 @@ def test_bf16_and_gated_entry_points_reject_before_any_launch(lib):
     f = lib.bsfa_prefill_bf16
     assert f(good, good, good, None, None, None, good, shape, 1, blk, None) == 1  # no output
     assert f(good, good, good, good + 8, None, None, good, shape, 1, blk, None) == 4  # bf16 out not 16-B aligned
-    assert f(None, None, None, None, None, None, None, S(N=1000), 1, blk, None) == 2
+    assert f(None, None, None, None, None, None, None, S(Hq=3, Hkv=2), 1, blk, None) == 2
     g = lib.bsfa_prefill_gated
     for bad_gate in (-1, 2, 7):  # unknown gate: shape status, before the pointer checks
         assert g(good, good, good, good, None, None, good, shape, 1, blk, bad_gate, None, None, None) == 2

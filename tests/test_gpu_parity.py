@@ -55,6 +55,18 @@ CASES = {
                                        "calib"),
     "bidirectional-odd-M": (dict(base="dit32k", batch=1, heads_q=2, heads_kv=2, seq_len=896, grid=(4, 7, 32)), 2,
                             "calib"),
+    # sequence lengths that are not a multiple of the tile (partial last block),
+    # through every route: head pairs, block pairs, one unit; both tile sizes
+    "ragged-headpair-causal": (dict(base="llama8k", seq_len=1000, heads_q=4, heads_kv=1), 3, "calib"),
+    "ragged-blockpair-bidirectional": (dict(base="llama8k", seq_len=1000, heads_q=3, heads_kv=1, causal=False), 2,
+                                       "calib"),
+    "ragged-one-unit-causal": (dict(base="llama8k", seq_len=700, heads_q=3, heads_kv=1), 2, "calib"),
+    "ragged-one-unit-bidirectional-d64-b64": (dict(base="tiny", seq_len=900, heads_q=2, heads_kv=2, causal=False),
+                                              2, "calib"),
+    "ragged-headpair-d64-b64": (dict(base="tiny", seq_len=1000), 4, "calib"),
+    "ragged-single-partial-tile": (dict(base="llama8k", seq_len=77, heads_q=2, heads_kv=1), None, "+inf"),
+    "ragged-dense-bidirectional": (dict(base="llama8k", seq_len=333, heads_q=2, heads_kv=2, causal=False), None,
+                                   "calib"),
 }
 
 
@@ -137,7 +149,8 @@ def test_deterministic_and_skipped_v_never_read():
     assert checked >= 2
 
 
-@pytest.mark.parametrize("name", ["llama-2k-G4-d128-b128", "dit-noncausal-b128", "tiny-d64-b64-batch2"])
+@pytest.mark.parametrize("name", ["llama-2k-G4-d128-b128", "dit-noncausal-b128", "tiny-d64-b64-batch2",
+                                  "ragged-headpair-causal", "ragged-one-unit-bidirectional-d64-b64"])
 def test_tile_max_pass(name):
     _gpu()
     w, data, thr = _make(name)

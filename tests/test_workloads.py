@@ -70,6 +70,8 @@ def test_dit_generator_small():
     assert np.mean(np.sum(qf[:, :, :-1] * qf[:, :, 1:], axis=-1)) > 0.4 * 64
 
 
-def test_unaligned_length_rejected():
-    with pytest.raises(ValueError):
-        wl.generate(wl.get_config("tiny", seq_len=1000), seed=0)
+def test_unaligned_length_has_a_partial_last_block():
+    w = wl.get_config("tiny", seq_len=1000)
+    d = wl.generate(w, seed=0)
+    assert w.n_blocks == 16 and d["q"].shape[2] == 1000
+    assert all(0 <= kp <= qp < 1000 for _, _, qp, kp in d["planted"])
