@@ -29,6 +29,7 @@ EXPORTED = (
     "bsfa_prefill_ex",
     "bsfa_prefill_bf16",
     "bsfa_prefill_gated",
+    "bsfa_prefill_varlen",
     "bsfa_tile_max",
     "bsfa_calibrate_fixed_k",
     "bsfa_calibrate_levels",
@@ -81,6 +82,8 @@ def load_library() -> ctypes.CDLL:
     lib.bsfa_prefill_bf16.restype = i32
     lib.bsfa_prefill_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, BsfaShape, i32, BsfaBlock, i32, vp, vp, vp]
     lib.bsfa_prefill_gated.restype = i32
+    lib.bsfa_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, BsfaShape, i32, BsfaBlock, vp, vp, vp, vp]
+    lib.bsfa_prefill_varlen.restype = i32
     lib.bsfa_calibrate_levels.argtypes = [vp, i64, i64, i64, i32, vp, i64, vp, vp]
     lib.bsfa_calibrate_levels.restype = i32
     lib.bsfa_tile_max.argtypes = [vp, vp, vp, BsfaShape, i32, BsfaBlock, vp]
@@ -212,6 +215,23 @@ def bsfa_prefill_gated(q, k, v, out, lse, skip_counts, thresholds, shape: BsfaSh
         raise BsfaError(st, "bsfa_prefill_gated")
 
 
+def bsfa_prefill_varlen(q, k, v, out, lse, skip_counts, thresholds, shape: BsfaShape, causal: int,
+                        block: BsfaBlock, seq_lens, tile_state=None, tile_max=None, stream=None) -> None:
+    """C ABI ``bsfa_prefill_varlen``: ``seq_lens`` is an int32 [B] device tensor (see include/bsfa.h)."""
+    st = bsfa_validate(shape, causal, block)
+    if st != BSFA_OK:
+        raise BsfaError(st, "bsfa_prefill_varlen")
+    _check_all(q, k, v, out, lse, skip_counts, thresholds, shape, block, tile_state, tile_max)
+    _check(seq_lens, "seq_lens", torch.int32, (shape.batch,), q.device)
+    if seq_lens is None:
+        raise ValueError("seq_lens is required")
+    st = load_library().bsfa_prefill_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(skip_counts), _ptr(thresholds),
+        shape, int(causal), block, _ptr(seq_lens), _ptr(tile_state), _ptr(tile_max), _stream(stream))
+    if st != BSFA_OK:
+        raise BsfaError(st, "bsfa_prefill_varlen")
+
+
 def bsfa_calibrate_levels(tile_max, n_samples: int, n_heads: int, n_blocks: int, causal: int, ks,
                           thresholds, stream=None) -> None:
     """C ABI ``bsfa_calibrate_levels``: ``ks`` is a host sequence of ints, ``thresholds``
@@ -282,6 +302,28 @@ def calibrate_levels(tile_maxima: torch.Tensor, ks, causal: bool, stream=None) -
     thr = torch.empty((len(ks), H, M), dtype=torch.float32, device=tile_maxima.device)
     bsfa_calibrate_levels(tile_maxima, S, H, M, int(causal), ks, thr, stream)
     return thr
+
+
+def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, thresholds: torch.Tensor, causal: bool,
+                   block: int, seq_lens: torch.Tensor, diagnostics: bool = False, stream=None) -> dict:
+    """Allocate the outputs and run ``bsfa_prefill_varlen`` (padded batch, int32 device lengths).
+    Entries past each sequence are left as allocated (torch.empty)."""
+    B, Hq, N, d = q.shape
+    shape = make_shape(B, Hq, k.shape[1], N, d, thresholds.shape[1])
+    blk = make_block(block)
+    M = -(-N // block)
+    dev = q.device
+    res = {
+        "out": torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev),
+        "lse": torch.empty((B, Hq, N), dtype=torch.float32, device=dev),
+        "skip_counts": torch.empty((B, Hq, M), dtype=torch.int32, device=dev),
+    }
+    if diagnostics:
+        res["tile_state"] = torch.empty((B, Hq, M, M), dtype=torch.uint8, device=dev)
+        res["tile_max"] = torch.empty((B, Hq, M, M), dtype=torch.float32, device=dev)
+    bsfa_prefill_varlen(q, k, v, res["out"], res["lse"], res["skip_counts"], thresholds, shape, int(causal), blk,
+                        seq_lens, res.get("tile_state"), res.get("tile_max"), stream)
+    return res
 
 
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, thresholds: torch.Tensor, causal: bool,

@@ -50,7 +50,8 @@ bsfa::FwdParams shape_params(const bsfa_shape& shape, const bsfa_block& block) {
 // out is fp32 unless out_bf16 is set (then out is null)
 int prefill_impl(const void* q, const void* k, const void* v, float* out, uint16_t* out_bf16, float* lse,
                  int32_t* skip_counts, const float* thresholds, bsfa_shape shape, int causal, bsfa_block block,
-                 int gate, uint8_t* tile_state, float* tile_max, int diagnostics, void* stream) {
+                 int gate, uint8_t* tile_state, float* tile_max, int diagnostics, void* stream,
+                 const int32_t* seq_lens = nullptr) {
   const int st = check_shape(shape, causal, block);
   if (st != BSFA_OK) return st;
   if (gate != BSFA_GATE_THRESHOLD && gate != BSFA_GATE_GAP) return BSFA_ERR_SHAPE;
@@ -58,7 +59,7 @@ int prefill_impl(const void* q, const void* k, const void* v, float* out, uint16
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out ? (const void*)out : out_bf16, 16))
     return BSFA_ERR_ALIGN;
   if (!aligned(thresholds, 4) || (lse && !aligned(lse, 4)) || (skip_counts && !aligned(skip_counts, 4)) ||
-      (tile_max && !aligned(tile_max, 4)))
+      (tile_max && !aligned(tile_max, 4)) || (seq_lens && !aligned(seq_lens, 4)))
     return BSFA_ERR_ALIGN;
 
   bsfa::FwdParams p = shape_params(shape, block);
@@ -73,6 +74,7 @@ int prefill_impl(const void* q, const void* k, const void* v, float* out, uint16
   p.thresholds = thresholds;
   p.tile_state = tile_state;
   p.tile_max = tile_max;
+  p.seq_lens = seq_lens;
   return bsfa::launch_fwd(p, (int)shape.head_dim, block.bm, causal, diagnostics,
                           static_cast<hipStream_t>(stream));
 }
@@ -120,6 +122,15 @@ int bsfa_prefill_gated(const void* q, const void* k, const void* v, float* out, 
   const int diagnostics = (tile_state || tile_max) ? 1 : 0;
   return prefill_impl(q, k, v, out, nullptr, lse, skip_counts, thresholds, shape, causal, block, gate, tile_state,
                       tile_max, diagnostics, stream);
+}
+
+int bsfa_prefill_varlen(const void* q, const void* k, const void* v, float* out, float* lse, int32_t* skip_counts,
+                        const float* thresholds, bsfa_shape shape, int causal, bsfa_block block,
+                        const int32_t* seq_lens, uint8_t* tile_state, float* tile_max, void* stream) {
+  if (!seq_lens) return BSFA_ERR_NULL;
+  const int diagnostics = (tile_state || tile_max) ? 1 : 0;
+  return prefill_impl(q, k, v, out, nullptr, lse, skip_counts, thresholds, shape, causal, block,
+                      BSFA_GATE_THRESHOLD, tile_state, tile_max, diagnostics, stream, seq_lens);
 }
 
 int bsfa_tile_max(const void* q, const void* k, float* tile_max, bsfa_shape shape, int causal, bsfa_block block,

@@ -213,6 +213,11 @@ __global__ void __launch_bounds__(BLK * 2) bsfa_fwd_kernel(const FwdParams p) {
   L /= p.B;
   const int i = CAUSAL ? (p.M - 1 - L) : L;  // causal: heaviest query blocks first
   const int hq = g * p.G + hin;
+  // length of this batch element's sequence (per-sequence lengths: clamped to
+  // [0, N]); a query block past its end has nothing to compute or write
+  const int n_seq = (RAGGED && p.seq_lens) ? min(max(p.seq_lens[b], 0), p.N) : p.N;
+  const int m_seq = RAGGED ? (n_seq + BLK - 1) / BLK : p.M;
+  if (RAGGED && i >= m_seq) return;
 
   const size_t q_head = (size_t)(b * p.Hq + hq) * p.N;
   const size_t kv_head = (size_t)(b * p.Hkv + g) * p.N;
@@ -233,7 +238,7 @@ __global__ void __launch_bounds__(BLK * 2) bsfa_fwd_kernel(const FwdParams p) {
   // ---- (a2) Q_i stays in registers: B operand of S^T = K Q^T --------------
   bf16x8 qf[C::KC];
   {
-    const u32x4* qg = reinterpret_cast<const u32x4*>(p.q) + (q_head + (RAGGED ? min(qrow, p.N - 1) : qrow)) * C::CPR;
+    const u32x4* qg = reinterpret_cast<const u32x4*>(p.q) + (q_head + (RAGGED ? min(qrow, n_seq - 1) : qrow)) * C::CPR;
 #pragma unroll
     for (int c = 0; c < C::KC; ++c) qf[c] = __builtin_bit_cast(bf16x8, qg[2 * c + hh]);
   }
@@ -242,7 +247,7 @@ __global__ void __launch_bounds__(BLK * 2) bsfa_fwd_kernel(const FwdParams p) {
   // threshold of (head, query block); blocks past the table reuse the last entry
   const float tau = MAXONLY ? INFINITY : p.thresholds[hq * p.T_len + min(i, p.T_len - 1)];
   const float c2 = p.scale_log2;
-  const int jend = CAUSAL ? i : p.M - 1;
+  const int jend = CAUSAL ? i : m_seq - 1;
   const size_t diag_row = ((size_t)(b * p.Hq + hq) * p.M + i) * p.M;
 
   f32x16 o[C::DB];
@@ -260,7 +265,7 @@ __global__ void __launch_bounds__(BLK * 2) bsfa_fwd_kernel(const FwdParams p) {
 #pragma unroll
   for (int it = 0; it < C::LD; ++it) {
     const int c = tid + C::NT * it;
-    kreg[it] = kg[RAGGED ? tile_chunk<C::CPR>(0, c, p.N) : c];
+    kreg[it] = kg[RAGGED ? tile_chunk<C::CPR>(0, c, n_seq) : c];
   }
 #pragma unroll
   for (int it = 0; it < C::LD; ++it) {
@@ -277,7 +282,7 @@ __global__ void __launch_bounds__(BLK * 2) bsfa_fwd_kernel(const FwdParams p) {
 #pragma unroll
       for (int it = 0; it < C::LD; ++it) {
         const int c = tid + C::NT * it;
-        kreg[it] = RAGGED ? kg[tile_chunk<C::CPR>((j + 1) * BLK, c, p.N)] : src[c];
+        kreg[it] = RAGGED ? kg[tile_chunk<C::CPR>((j + 1) * BLK, c, n_seq)] : src[c];
       }
     }
     // ---- (a4) S^T = K_j Q_i^T on MFMA --------------------------------------
@@ -294,7 +299,7 @@ __global__ void __launch_bounds__(BLK * 2) bsfa_fwd_kernel(const FwdParams p) {
         }
     }
     if (RAGGED) {
-      const int rows_left = p.N - i * BLK, keys_left = p.N - j * BLK;
+      const int rows_left = n_seq - i * BLK, keys_left = n_seq - j * BLK;
       if (rows_left < BLK || keys_left < BLK) mask_tail(s, qloc, hh, rows_left, keys_left);
     }
     // ---- (a5) tile maximum and gate ---------------------------------------
@@ -329,7 +334,7 @@ __global__ void __launch_bounds__(BLK * 2) bsfa_fwd_kernel(const FwdParams p) {
 #pragma unroll
       for (int it = 0; it < C::LD; ++it) {
         const int c = tid + C::NT * it;
-        vreg[it] = RAGGED ? vg[tile_chunk<C::CPR>(j * BLK, c, p.N)] : src[c];
+        vreg[it] = RAGGED ? vg[tile_chunk<C::CPR>(j * BLK, c, n_seq)] : src[c];
       }
     }
     // K_{j+1} -> LDS (every wave has finished reading K_j)
@@ -409,20 +414,20 @@ __global__ void __launch_bounds__(BLK * 2) bsfa_fwd_kernel(const FwdParams p) {
   }
 
   if (MAXONLY) {
-    if (CAUSAL)
-      for (int jj = i + 1 + tid; jj < p.M; jj += C::NT) p.tile_max[diag_row + jj] = __builtin_nanf("");
+    if (CAUSAL || RAGGED)
+      for (int jj = jend + 1 + tid; jj < p.M; jj += C::NT) p.tile_max[diag_row + jj] = __builtin_nanf("");
     return;
   }
   // ---- (a9) epilogue: O_i = O_acc / l, lse, skip count -------------------
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.f / (lb_run + __shfl_xor(lb_run, 32));
-  if (!RAGGED || qrow < p.N) {
+  if (!RAGGED || qrow < n_seq) {
     store_out_row(p, q_head + qrow, o, inv, hh);
     if (p.lse && hh == 0) p.lse[q_head + qrow] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
   }
   if (p.skip_counts && tid == 0) p.skip_counts[(size_t)(b * p.Hq + hq) * p.M + i] = nskip;
-  if (DIAG_OUT && CAUSAL) {
-    for (int jj = i + 1 + tid; jj < p.M; jj += C::NT) {
+  if (DIAG_OUT && (CAUSAL || RAGGED)) {
+    for (int jj = jend + 1 + tid; jj < p.M; jj += C::NT) {
       if (p.tile_state) p.tile_state[diag_row + jj] = 0;
       if (p.tile_max) p.tile_max[diag_row + jj] = __builtin_nanf("");
     }
@@ -516,6 +521,13 @@ __global__ void __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2,
   }
   const int hq = hq_u[u];
   const int i = i_u[u];
+  // per-sequence length (see the one-unit kernel).  A block pair whose second
+  // block lies past the end keeps that unit running through the barriers; it
+  // writes nothing
+  const int n_seq = (RAGGED && p.seq_lens) ? min(max(p.seq_lens[b], 0), p.N) : p.N;
+  const int m_seq = RAGGED ? (n_seq + BLK - 1) / BLK : p.M;
+  if (RAGGED && i_u[0] >= m_seq) return;  // both units past the end (i_u[0] <= i_u[1])
+  const bool live = !RAGGED || i < m_seq;
   const size_t q_head = (size_t)(b * p.Hq + hq) * p.N;
   const size_t kv_head = (size_t)(b * p.Hkv + g) * p.N;
   const int qloc = 32 * wu + l32;
@@ -537,7 +549,7 @@ __global__ void __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
     for (int it = 0; it < P2::LD; ++it) {
       const int c = tid + P2::NT * it;
-      qr[it] = RAGGED ? qh[tile_chunk<C::CPR>(i_u[uu] * BLK, c, p.N)] : qg[c];
+      qr[it] = RAGGED ? qh[tile_chunk<C::CPR>(i_u[uu] * BLK, c, n_seq)] : qg[c];
     }
 #pragma unroll
     for (int it = 0; it < P2::LD; ++it) {
@@ -553,7 +565,7 @@ __global__ void __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2,
   for (int uu = 0; uu < 2; ++uu)
     tau_u[uu] = MAXONLY ? INFINITY : p.thresholds[hq_u[uu] * p.T_len + min(i_u[uu], p.T_len - 1)];
   const float c2 = p.scale_log2;
-  const int jend = CAUSAL ? i : p.M - 1;  // identical for both units
+  const int jend = CAUSAL ? i : m_seq - 1;  // identical for both units
   const size_t diag_row = ((size_t)(b * p.Hq + hq) * p.M + i) * p.M;
 
   f32x16 o[C::DB];
@@ -570,7 +582,7 @@ __global__ void __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
   for (int it = 0; it < P2::LD; ++it) {
     const int c = tid + P2::NT * it;
-    kreg[it] = kg[RAGGED ? tile_chunk<C::CPR>(0, c, p.N) : c];
+    kreg[it] = kg[RAGGED ? tile_chunk<C::CPR>(0, c, n_seq) : c];
   }
 #pragma unroll
   for (int it = 0; it < P2::LD; ++it) {
@@ -590,7 +602,7 @@ __global__ void __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
       for (int it = 0; it < P2::LD; ++it) {
         const int c = tid + P2::NT * it;
-        kreg[it] = RAGGED ? kg[tile_chunk<C::CPR>((j + 1) * BLK, c, p.N)] : src[c];
+        kreg[it] = RAGGED ? kg[tile_chunk<C::CPR>((j + 1) * BLK, c, n_seq)] : src[c];
       }
     }
     // ---- (a4) S^T = K_j Q^T ------------------------------------------------
@@ -606,7 +618,7 @@ __global__ void __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2,
         }
     }
     if constexpr (RAGGED) {
-      const int rows_left = p.N - i * BLK, keys_left = p.N - j * BLK;
+      const int rows_left = n_seq - i * BLK, keys_left = n_seq - j * BLK;
       if (rows_left < BLK || keys_left < BLK) mask_tail(s, qloc, hh, rows_left, keys_left);
     }
     // ---- (a5) tile maxima of both units and their gates ---------------------
@@ -633,7 +645,7 @@ __global__ void __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2,
       for (int ww = 1; ww < P2::NWU; ++ww) tm = fmaxf(tm, red[uu][ww]);
       const float tms = tm * p.scale;
       skip_of[uu] = MAXONLY ? 1 : gate_skip(p.gate, j != i_u[uu], tms, tau_u[uu], mrun_u[uu]);
-      if (DIAG_OUT && uu == u && wu == 0 && lane == 0) {
+      if (DIAG_OUT && uu == u && wu == 0 && lane == 0 && live) {
         if (p.tile_state) p.tile_state[diag_row + j] = (j == i) ? 3 : (skip_of[uu] ? 2 : 1);
         if (p.tile_max) p.tile_max[diag_row + j] = tms;
       }
@@ -646,7 +658,7 @@ __global__ void __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
       for (int it = 0; it < P2::LD; ++it) {
         const int c = tid + P2::NT * it;
-        vreg[it] = RAGGED ? vg[tile_chunk<C::CPR>(j * BLK, c, p.N)] : src[c];
+        vreg[it] = RAGGED ? vg[tile_chunk<C::CPR>(j * BLK, c, n_seq)] : src[c];
       }
     }
     if (more) {
@@ -728,20 +740,20 @@ __global__ void __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2,
   const int utid = wu * 64 + lane;  // thread index inside the unit
   constexpr int UNT = P2::NWU * 64;
   if (MAXONLY) {
-    if (CAUSAL)
-      for (int jj = i + 1 + utid; jj < p.M; jj += UNT) p.tile_max[diag_row + jj] = __builtin_nanf("");
+    if ((CAUSAL || RAGGED) && live)
+      for (int jj = jend + 1 + utid; jj < p.M; jj += UNT) p.tile_max[diag_row + jj] = __builtin_nanf("");
     return;
   }
   // ---- (a9) epilogue -------------------------------------------------------
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.f / (lb_run + __shfl_xor(lb_run, 32));
-  if (!RAGGED || qrow < p.N) {
+  if (!RAGGED || qrow < n_seq) {
     store_out_row(p, q_head + qrow, o, inv, hh);
     if (p.lse && hh == 0) p.lse[q_head + qrow] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
   }
-  if (p.skip_counts && utid == 0) p.skip_counts[(size_t)(b * p.Hq + hq) * p.M + i] = nskip;
-  if (DIAG_OUT && CAUSAL) {
-    for (int jj = i + 1 + utid; jj < p.M; jj += UNT) {
+  if (p.skip_counts && utid == 0 && live) p.skip_counts[(size_t)(b * p.Hq + hq) * p.M + i] = nskip;
+  if (DIAG_OUT && (CAUSAL || RAGGED) && live) {
+    for (int jj = jend + 1 + utid; jj < p.M; jj += UNT) {
       if (p.tile_state) p.tile_state[diag_row + jj] = 0;
       if (p.tile_max) p.tile_max[diag_row + jj] = __builtin_nanf("");
     }
@@ -778,11 +790,12 @@ static int launch_units_r(const FwdParams& p, hipStream_t s) {
   return launch_one<D, BLK, CAUSAL, DIAG_OUT, MAXONLY, RAGGED>(p, s);
 }
 
-// A sequence length that is not a multiple of the tile selects the kernels
-// compiled with the tail handling; aligned lengths run without it.
+// A sequence length that is not a multiple of the tile, or per-sequence
+// lengths, select the kernels compiled with the tail handling; aligned
+// lengths run without it.
 template <int D, int BLK, bool CAUSAL, bool DIAG_OUT, bool MAXONLY>
 static int launch_units(const FwdParams& p, hipStream_t s) {
-  if (p.N % BLK) return launch_units_r<D, BLK, CAUSAL, DIAG_OUT, MAXONLY, true>(p, s);
+  if (p.N % BLK || p.seq_lens) return launch_units_r<D, BLK, CAUSAL, DIAG_OUT, MAXONLY, true>(p, s);
   return launch_units_r<D, BLK, CAUSAL, DIAG_OUT, MAXONLY, false>(p, s);
 }
 

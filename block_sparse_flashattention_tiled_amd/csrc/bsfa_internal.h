@@ -18,6 +18,7 @@ struct FwdParams {
   const float* thresholds;  // fp32 [Hq, T_len]
   uint8_t* tile_state;      // uint8 [B, Hq, M, M] or null (diagnostic launches only)
   float* tile_max;          // fp32 [B, Hq, M, M] or null (diagnostic launches only)
+  const int32_t* seq_lens;  // int32 [B] or null: per-sequence lengths (each clamped to [0, N])
   int B, Hq, Hkv, G, N, M, T_len;
   float scale;       // 1 / sqrt(d)
   float scale_log2;  // scale * log2(e)

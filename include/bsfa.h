@@ -157,6 +157,27 @@ int bsfa_prefill_gated(const void* q, const void* k, const void* v, float* out, 
                        uint8_t* tile_state, float* tile_max, void* stream);
 
 /*
+ * bsfa_prefill_varlen - a batch of sequences of different lengths, each
+ * attended independently (the mixed-length workload of Sec. 5.2,
+ * "Variable-length analysis").
+ *  q, k, v, out, lse  laid out as for bsfa_prefill with N = shape.seq_len the
+ *              longest (padded) length: sequence b occupies positions
+ *              [0, seq_lens[b]) of its rows.
+ *  seq_lens    int32 [B] DEVICE array, required: the length of each sequence;
+ *              values are clamped to [0, N].
+ *  Sequence b is computed exactly as bsfa_prefill would compute it alone at
+ *  length seq_lens[b] (partial last block, positions past it do not exist),
+ *  with the same threshold table.  Rows of out / lse past seq_lens[b], counts
+ *  of query blocks past its last block, and the diagnostics of those blocks
+ *  are not written; diagnostics of key blocks past its last block read as not
+ *  computed (BSFA_TILE_PRUNED, NaN).
+ *  tile_state, tile_max  optional diagnostics as for bsfa_prefill_ex.
+ */
+int bsfa_prefill_varlen(const void* q, const void* k, const void* v, float* out, float* lse, int32_t* skip_counts,
+                        const float* thresholds, bsfa_shape shape, int causal, bsfa_block block,
+                        const int32_t* seq_lens, uint8_t* tile_state, float* tile_max, void* stream);
+
+/*
  * bsfa_tile_max - calibration pass: the tile maxima alone.
  *  q, k      as for bsfa_prefill
  *  tile_max  fp32 [B, H_q, M, M]: max over the visible entries of each computed
