@@ -13,6 +13,15 @@ library's own calibration pass (tile maxima + fixed-k selection on the GPU),
 outside the timed region.  Launch times are taken with HIP events on the
 stream the kernels run on.
 
+Also reported, outside ``value``:
+  * ``long_context``: the 128K GQA layer (32 query heads over 4 KV heads) at
+    threshold -inf and at its ~95% fixed-k point, timed the same way
+    (``--no-128k`` skips it);
+  * ``gate_study``: on the 32K inputs, the fixed-k points next to the gap gate
+    (skip a tile below the running maximum minus a gap) at several gaps -
+    realised skip fraction, time and error against the dense output
+    (``--no-gate-study`` skips it).
+
 Prints one JSON line.  ``--gpus N`` with N > 1 exits: this build runs on one GPU.
 """
 
@@ -30,6 +39,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
+GAP_SWEEP = (1.0, 2.0, 3.0, 4.5, 6.0)  # gaps of the gate study, scaled-score units
 
 
 def log(msg):
@@ -101,6 +111,110 @@ def cpu_baseline(data, w, ks, budget_s):
     }
 
 
+class Layer:
+    """Resident inputs, calibration and output buffers of one workload."""
+
+    def __init__(self, name, seed, torch, bb, wl, acc):
+        self.torch, self.bb, self.acc = torch, bb, acc
+        self.w = w = wl.get_config(name)
+        log(f"generating {w.name}: B={w.batch} Hq={w.heads_q} Hkv={w.heads_kv} N={w.seq_len} d={w.head_dim}")
+        t0 = time.time()
+        self.data = wl.generate(w, seed=seed)
+        log(f"generated in {time.time() - t0:.1f} s; uploading")
+        self.q, self.k, self.v = (bb.bits_to_device(self.data[n]) for n in ("q", "k", "v"))
+        self.M = w.n_blocks
+        self.shape = bb.make_shape(w.batch, w.heads_q, w.heads_kv, w.seq_len, w.head_dim, self.M)
+        self.block = bb.make_block(w.block)
+        self.tmax = bb.tile_max(self.q, self.k, w.causal, w.block)  # calibration pass (untimed)
+        self.out = torch.empty((w.batch, w.heads_q, w.seq_len, w.head_dim), dtype=torch.float32, device="cuda")
+        self.lse = torch.empty((w.batch, w.heads_q, w.seq_len), dtype=torch.float32, device="cuda")
+        self.stream = torch.cuda.current_stream()
+
+    def fixed_k_points(self, targets):
+        points = []
+        for tgt in targets:
+            kk = self.acc.k_for_target(self.M, tgt, self.w.causal)
+            thr = self.bb.calibrate_fixed_k(self.tmax, kk, self.w.causal)
+            points.append({"target": tgt, "k": kk, "thr": thr, "gate": "threshold"})
+        return points
+
+    def launch(self, pt, counts, out=None):
+        w, bb = self.w, self.bb
+        out = self.out if out is None else out
+        if pt["gate"] == "threshold":
+            bb.bsfa_prefill(self.q, self.k, self.v, out, self.lse, counts, pt["thr"], self.shape, int(w.causal),
+                            self.block, self.stream)
+        else:
+            bb.bsfa_prefill_gated(self.q, self.k, self.v, out, self.lse, counts, pt["thr"], self.shape,
+                                  int(w.causal), self.block, bb.GATES[pt["gate"]], None, None, self.stream)
+
+    def measure(self, points, steps, warmup):
+        """Time every point ``steps`` times (HIP events around each launch on the
+        launching stream); fill per-point statistics.  Returns the step time."""
+        torch, acc, w = self.torch, self.acc, self.w
+        counts = [torch.empty((w.batch, w.heads_q, self.M), dtype=torch.int32, device="cuda") for _ in points]
+        log(f"{w.name}: warmup {warmup} steps x {len(points)} launches")
+        for _ in range(warmup):
+            for pi, pt in enumerate(points):
+                self.launch(pt, counts[pi])
+        torch.cuda.synchronize()
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in points]
+              for _ in range(steps)]
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_start.record(self.stream)
+        for s in range(steps):
+            for pi, pt in enumerate(points):
+                ev[s][pi][0].record(self.stream)
+                self.launch(pt, counts[pi])
+                ev[s][pi][1].record(self.stream)
+        t_end.record(self.stream)
+        torch.cuda.synchronize()
+        total_ms = t_start.elapsed_time(t_end)
+        log(f"{w.name}: timed {steps} steps in {total_ms:.1f} ms")
+        M, blk, d = self.M, w.block, w.head_dim
+        dense_flops = acc.dense_equivalent_flops(w.batch, w.heads_q, M, blk, d, w.causal)
+        computed = acc.computed_tiles(M, w.causal) * w.batch * w.heads_q
+        for pi, pt in enumerate(points):
+            durs = [ev[s][pi][0].elapsed_time(ev[s][pi][1]) for s in range(steps)]
+            skipped = int(counts[pi].sum().item())
+            fl = acc.executed_flops(w.batch, w.heads_q, M, blk, d, skipped, w.causal)
+            pt.update(ms_mean=float(np.mean(durs)), ms_median=float(np.median(durs)), ms_min=float(np.min(durs)),
+                      skipped_tiles=skipped, skip_fraction=skipped / computed, executed_flops=fl)
+            if pt.get("k") is not None or pt["gate"] == "threshold":
+                pt["designed_skip_fraction"] = (acc.designed_skip_fraction(M, pt["k"], w.causal)
+                                                if pt.get("k") is not None else 0.0)
+            pt["executed_tflops"] = fl / (pt["ms_mean"] * 1e-3) / 1e12
+            pt["dense_equivalent_tflops"] = dense_flops / (pt["ms_mean"] * 1e-3) / 1e12
+        return total_ms / steps
+
+    def errors_vs(self, ref_out, ref_lse, pt):
+        """Error of one point's output against a reference output (same inputs)."""
+        torch, w = self.torch, self.w
+        counts = torch.empty((w.batch, w.heads_q, self.M), dtype=torch.int32, device="cuda")
+        out = torch.empty_like(self.out)
+        self.launch(pt, counts, out)
+        torch.cuda.synchronize()
+        diff = (out - ref_out).double()
+        rel = float(diff.norm() / ref_out.double().norm())
+        return {"rel_l2_out": rel, "max_abs_out": float(diff.abs().max()),
+                "mean_abs_lse": float((self.lse - ref_lse).abs().double().mean())}
+
+
+def public(points):
+    return [{kk: vv for kk, vv in pt.items() if kk != "thr"} for pt in points]
+
+
+def speedups(points):
+    dense_ms = points[0]["ms_mean"]
+    for pt in points:
+        f = pt["skip_fraction"]
+        pt["speedup_vs_dense"] = dense_ms / pt["ms_mean"]
+        pt["flop_ratio"] = 2.0 / (2.0 - f)
+        pt["speedup_floor"] = 0.8 * pt["flop_ratio"]
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,6 +224,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle baseline budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-128k", action="store_true", help="skip the 128K long-context leg")
+    ap.add_argument("--no-gate-study", action="store_true", help="skip the gap-gate comparison")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="also run one plain 1 GiB device copy, whose HBM counters calibrate the kernel's")
     args = ap.parse_args()
@@ -129,39 +245,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     bb.load_library()
-    w = wl.get_config(args.workload)
-    log(f"generating {w.name}: B={w.batch} Hq={w.heads_q} Hkv={w.heads_kv} N={w.seq_len} d={w.head_dim}")
-    t0 = time.time()
-    data = wl.generate(w, seed=args.seed)
-    log(f"generated in {time.time() - t0:.1f} s; uploading")
-    q = bb.bits_to_device(data["q"])
-    k = bb.bits_to_device(data["k"])
-    v = bb.bits_to_device(data["v"])
-    M, blk, d = w.n_blocks, w.block, w.head_dim
 
-    # calibration (outside the timed region): tile maxima, then fixed-k tables
-    tmax = bb.tile_max(q, k, w.causal, blk)
-    points = []
+    # ---- the headline workload -------------------------------------------------
+    lay = Layer(args.workload, args.seed, torch, bb, wl, acc)
+    w = lay.w
     targets = list(w.skip_targets)
     if 0.0 not in targets:
         targets = [0.0] + targets  # the dense reference for speedups
-    for tgt in targets:
-        kk = acc.k_for_target(M, tgt, w.causal)
-        thr = bb.calibrate_fixed_k(tmax, kk, w.causal)
-        points.append({"target": tgt, "k": kk, "thr": thr})
+    points = lay.fixed_k_points(targets)
     torch.cuda.synchronize()
-    del tmax
-
-    shape = bb.make_shape(w.batch, w.heads_q, w.heads_kv, w.seq_len, d, M)
-    block = bb.make_block(blk)
-    out = torch.empty((w.batch, w.heads_q, w.seq_len, d), dtype=torch.float32, device="cuda")
-    lse = torch.empty((w.batch, w.heads_q, w.seq_len), dtype=torch.float32, device="cuda")
-    counts = [torch.empty((w.batch, w.heads_q, M), dtype=torch.int32, device="cuda") for _ in points]
-    stream = torch.cuda.current_stream()
-
-    def launch(pi):
-        bb.bsfa_prefill(q, k, v, out, lse, counts[pi], points[pi]["thr"], shape, int(w.causal), block, stream)
-
     if args.traffic_probe:
         # a copy of known size: reads 1 GiB and writes 1 GiB; profiling counters
         # taken in the same run are scaled by what this copy reports
@@ -170,66 +262,16 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b
-    log(f"warmup {args.warmup} steps x {len(points)} launches")
-    for _ in range(args.warmup):
-        for pi in range(len(points)):
-            launch(pi)
-    torch.cuda.synchronize()
-
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in points]
-          for _ in range(args.steps)]
-    step_start = torch.cuda.Event(enable_timing=True)
-    step_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    step_start.record(stream)
-    for s in range(args.steps):
-        for pi in range(len(points)):
-            ev[s][pi][0].record(stream)
-            launch(pi)
-            ev[s][pi][1].record(stream)
-    step_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = step_start.elapsed_time(step_end)
-    log(f"timed {args.steps} steps in {total_ms:.1f} ms")
-
-    dense_flops = acc.dense_equivalent_flops(w.batch, w.heads_q, M, blk, d, w.causal)
-    computed = acc.computed_tiles(M, w.causal) * w.batch * w.heads_q
-    step_flops = 0
-    sum_dur = 0.0
-    for pi, pt in enumerate(points):
-        durs = [ev[s][pi][0].elapsed_time(ev[s][pi][1]) for s in range(args.steps)]
-        skipped = int(counts[pi].sum().item())
-        fl = acc.executed_flops(w.batch, w.heads_q, M, blk, d, skipped, w.causal)
-        pt.update(
-            ms_mean=float(np.mean(durs)),
-            ms_median=float(np.median(durs)),
-            ms_min=float(np.min(durs)),
-            skipped_tiles=skipped,
-            skip_fraction=skipped / computed,
-            designed_skip_fraction=(acc.designed_skip_fraction(M, pt["k"], w.causal) if pt["k"] is not None
-                                    else 0.0),
-            executed_flops=fl,
-        )
-        pt["executed_tflops"] = fl / (pt["ms_mean"] * 1e-3) / 1e12
-        pt["dense_equivalent_tflops"] = dense_flops / (pt["ms_mean"] * 1e-3) / 1e12
-        if pt["target"] in w.skip_targets:
-            step_flops += fl
-            sum_dur += pt["ms_mean"]
-    dense_ms = points[0]["ms_mean"]
-    for pt in points:
-        f = pt["skip_fraction"]
-        pt["speedup_vs_dense"] = dense_ms / pt["ms_mean"]
-        pt["flop_ratio"] = 2.0 / (2.0 - f)
-        pt["speedup_floor"] = 0.8 * pt["flop_ratio"]
-
+    step_ms = lay.measure(points, args.steps, args.warmup)
+    speedups(points)
     timed = [pt for pt in points if pt["target"] in w.skip_targets]
-    step_ms = total_ms / args.steps
-    # the step also contains the dense reference launch when the sweep lacks it
-    value = step_flops * args.steps / (total_ms * 1e-3) / 1e12 if len(timed) == len(points) else \
+    step_flops = sum(pt["executed_flops"] for pt in timed)
+    sum_dur = sum(pt["ms_mean"] for pt in timed)
+    # the step also holds the dense reference launch when the sweep lacks it
+    value = step_flops / (step_ms * 1e-3) / 1e12 if len(timed) == len(points) else \
         step_flops / (sum_dur * 1e-3) / 1e12
     achieved = step_flops / (sum_dur * 1e-3) / 1e12  # algorithmic FLOPs per launch / mean launch time
 
-    traffic = measured_traffic(w.name)
     res = {
         "metric": "prefill attention executed TFLOP/s + speedup vs dense at 32K/128K, bf16",
         "value": value,
@@ -249,26 +291,65 @@ def main():
             "heads_q": w.heads_q,
             "heads_kv": w.heads_kv,
             "seq_len": w.seq_len,
-            "head_dim": d,
-            "block": blk,
+            "head_dim": w.head_dim,
+            "block": w.block,
             "causal": w.causal,
             "skip_targets": list(w.skip_targets),
             "thresholds": "fixed-k, self-calibrated on the GPU (bsfa_tile_max + bsfa_calibrate_fixed_k)",
         },
-        "points": [{kk: vv for kk, vv in pt.items() if kk != "thr"} for pt in points],
+        "points": public(points),
         "roofline": {
             "bound": "mfma",
             "achieved": achieved,
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS,
-            "traffic": traffic,
+            "traffic": measured_traffic(w.name),
         },
     }
+
+    # ---- gap gate next to the fixed-k table on the same inputs -----------------
+    if not args.no_gate_study:
+        ref_out = lay.out.clone()
+        lay.launch(points[0], torch.empty((w.batch, w.heads_q, lay.M), dtype=torch.int32, device="cuda"), ref_out)
+        torch.cuda.synchronize()
+        ref_lse = lay.lse.clone()
+        study = [dict(pt, gate="threshold") for pt in points[1:]]
+        for gap in GAP_SWEEP:
+            study.append({"target": None, "k": None, "gap": gap, "gate": "gap",
+                          "thr": torch.full((w.heads_q, lay.M), gap, dtype=torch.float32, device="cuda")})
+        lay.measure(study, max(3, args.steps // 4), 1)
+        for pt in study:
+            pt.update(lay.errors_vs(ref_out, ref_lse, pt))
+            pt["speedup_vs_dense"] = points[0]["ms_mean"] / pt["ms_mean"]
+        res["gate_study"] = {
+            "workload": w.name,
+            "reference": "the same kernel at threshold -inf",
+            "gap_gate": "skip tile j iff its maximum scaled score < (largest maximum of the kept tiles) - gap",
+            "points": public(study),
+        }
+        del ref_out
+
     if not args.no_cpu_baseline:
         log(f"CPU oracle baseline, ~{args.cpu_seconds:.0f} s")
         ks = [pt["k"] for pt in timed]
-        res["cpu_baseline"] = cpu_baseline(data, w, ks, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(lay.data, w, ks, args.cpu_seconds)
+    del lay
+    torch.cuda.empty_cache()
+
+    # ---- the 128K long-context layer ---------------------------------------------
+    if not args.no_128k and args.workload != "gqa128k":
+        big = Layer("gqa128k", args.seed, torch, bb, wl, acc)
+        bpts = big.fixed_k_points([0.0] + list(big.w.skip_targets))
+        big.measure(bpts, max(3, args.steps // 4), 1)
+        speedups(bpts)
+        res["long_context"] = {
+            "workload": big.w.name,
+            "batch": big.w.batch, "heads_q": big.w.heads_q, "heads_kv": big.w.heads_kv,
+            "seq_len": big.w.seq_len, "head_dim": big.w.head_dim, "block": big.w.block, "causal": big.w.causal,
+            "points": public(bpts),
+        }
+        del big
     print(json.dumps(res), flush=True)
 
 
