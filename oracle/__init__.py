@@ -5,9 +5,11 @@ baseline leg of ``bench.py`` may import this package.  The HIP product path
 never imports, links or executes it.  Every function cites the passage of
 "Block Sparse Flash Attention" (paperpeel.com/paper/2512.07011) it follows.
 
-Pins: each function here is checked by ``tests/test_oracle_pins.py`` against
-something other than itself (a library attention routine, closed forms,
-a brute-force streaming loop, invariants and the pages' printed figures).
+Pins: each function here is checked by the ``tests/test_oracle_*.py`` files
+against something other than itself (a library attention routine, closed
+forms, a brute-force streaming loop, invariants and the pages' printed
+figures); ``tests/test_oracle_mutants.py`` plants mistakes to show the pins
+catch them.
 """
 
 from .bsfa_oracle import *  # noqa: F401,F403

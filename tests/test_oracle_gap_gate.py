@@ -103,12 +103,12 @@ def test_decisions_invariant_under_a_common_shift():
         i = int(rng.integers(0, n))
         row = rng.normal(0, 3, n)
         gap = float(rng.uniform(0, 4))
-        base = oracle.gate_gap(row, i, gap)
+        base = oracle.gate_gap(row, [i], gap)
         for c in (-7.25, 3.5, 120.0):  # exact shifts in binary: no rounding flips a comparison
-            assert (oracle.gate_gap(row + c, i, gap) == base).all()
+            assert (oracle.gate_gap(row + c, [i], gap) == base).all()
         # the stored-threshold gate is not shift invariant, so this is a property of the gap reading
     row = np.array([0.0, 2.0, 1.0])
-    assert oracle.gate(row, 2, 0.5).tolist() != oracle.gate(row + 3.0, 2, 0.5).tolist()
+    assert oracle.gate(row, [2], 0.5).tolist() != oracle.gate(row + 3.0, [2], 0.5).tolist()
 
 
 def test_larger_gap_never_skips_more():
@@ -118,7 +118,7 @@ def test_larger_gap_never_skips_more():
         i = int(rng.integers(0, n))
         row = rng.normal(0, 2, n)
         gaps = np.sort(rng.uniform(-1, 5, 4))
-        skips = [oracle.gate_gap(row, i, g) for g in gaps]
+        skips = [oracle.gate_gap(row, [i], g) for g in gaps]
         for a, b in zip(skips, skips[1:]):
             assert not (b & ~a).any()
         assert not skips[0][i] and not skips[-1][i]  # diagonal bypass

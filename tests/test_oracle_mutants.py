@@ -13,15 +13,16 @@ import oracle
 from oracle import bsfa_oracle as ob
 import test_oracle_gap_gate as gap_pins
 import test_oracle_pins as pins
+import test_oracle_rect as rect_pins
 
 
-def _mut_gate_le(tile_max_row, i, tau):  # '<=' instead of the strict '<'
+def _mut_gate_le(tile_max_row, diag, tau):  # '<=' instead of the strict '<'
     skip = tile_max_row <= tau
-    skip[i] = False
+    skip[list(diag)] = False
     return skip
 
 
-def _mut_gate_no_bypass(tile_max_row, i, tau):  # diagonal gated like the rest
+def _mut_gate_no_bypass(tile_max_row, diag, tau):  # diagonal gated like the rest
     return tile_max_row < tau
 
 
@@ -55,22 +56,40 @@ def _mut_gqa_modulo(q, k, v, thresholds, causal, block, blocks, skip_override=No
     return res
 
 
-def _mut_gap_global_max(tile_max_row, i, tau):  # reference = max over every tile, not the running max
+def _mut_gap_global_max(tile_max_row, diag, tau):  # reference = max over every tile, not the running max
     skip = tile_max_row < np.max(tile_max_row) - tau
-    skip[i] = False
+    skip[list(diag)] = False
     return skip
 
 
-def _mut_gap_sign(tile_max_row, i, tau):  # M + tau instead of M - tau
+def _mut_gap_sign(tile_max_row, diag, tau):  # M + tau instead of M - tau
     n = tile_max_row.shape[0]
     skip = np.zeros(n, dtype=bool)
     m = -np.inf
     for j in range(n):
-        if j != i and tile_max_row[j] < m + tau:
+        if j not in diag and tile_max_row[j] < m + tau:
             skip[j] = True
         else:
             m = max(m, float(tile_max_row[j]))
     return skip
+
+
+def _mut_diag_square(i, bm, bn, m_kv):  # diagonal = same block index, as if the tile were square
+    return [i] if i < m_kv else []
+
+
+def _mut_diag_touching(i, bm, bn, m_kv):  # blocks that merely touch the query block count as diagonal
+    return [j for j in range(m_kv) if j * bn <= (i + 1) * bm and (j + 1) * bn >= i * bm]
+
+
+def _mut_calib_square(tile_max_row, i, k, causal, block=1):  # off-diagonal set of a square tile
+    cols = [j for j in (range(i) if causal else range(tile_max_row.shape[0])) if j != i]
+    if len(cols) <= k:
+        return -np.inf
+    if k == 0:
+        return np.inf
+    vals = np.sort(tile_max_row[cols])[::-1]
+    return 0.5 * (vals[k - 1] + vals[k])
 
 
 MUTANTS = [
@@ -84,6 +103,11 @@ MUTANTS = [
     ("gate_gap", _mut_gap_global_max,
      lambda: gap_pins.test_gap_gate_matches_brute_force_streaming(True, 1, 2, 1, 256, 16, 4, 21)),
     ("gate_gap", _mut_gap_sign, lambda: gap_pins.test_uniform_scores_closed_form(True)),
+    ("diagonal_blocks", _mut_diag_square,
+     lambda: rect_pins.test_infinite_threshold_keeps_the_tiles_sharing_a_position(True, 256, (64, 32))),
+    ("diagonal_blocks", _mut_diag_touching,
+     lambda: rect_pins.test_infinite_threshold_keeps_the_tiles_sharing_a_position(False, 256, (32, 64))),
+    ("calibrate_row", _mut_calib_square, lambda: rect_pins.test_rect_fixed_k_keeps_exactly_k(True, (64, 32))),
 ]
 
 
