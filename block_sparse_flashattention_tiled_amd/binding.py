@@ -33,6 +33,7 @@ EXPORTED = (
     "bsfa_tile_max",
     "bsfa_calibrate_fixed_k",
     "bsfa_calibrate_levels",
+    "bsfa_calibrate",
     "bsfa_validate",
     "bsfa_status_string",
 )
@@ -90,6 +91,8 @@ def load_library() -> ctypes.CDLL:
     lib.bsfa_tile_max.restype = i32
     lib.bsfa_calibrate_fixed_k.argtypes = [vp, i64, i64, i64, i32, i64, vp, vp]
     lib.bsfa_calibrate_fixed_k.restype = i32
+    lib.bsfa_calibrate.argtypes = [vp, BsfaShape, i32, BsfaBlock, vp, i64, vp, vp]
+    lib.bsfa_calibrate.restype = i32
     lib.bsfa_validate.argtypes = [BsfaShape, i32, BsfaBlock]
     lib.bsfa_validate.restype = i32
     lib.bsfa_status_string.argtypes = [i32]
@@ -104,6 +107,20 @@ def make_shape(batch, n_heads_q, n_heads_kv, seq_len, head_dim, thr_len) -> Bsfa
 
 def make_block(bm: int, bn: Optional[int] = None) -> BsfaBlock:
     return BsfaBlock(bm, bm if bn is None else bn)
+
+
+def as_block(block) -> BsfaBlock:
+    """A BsfaBlock from an int (square tile), a (bm, bn) pair or a BsfaBlock."""
+    if isinstance(block, BsfaBlock):
+        return block
+    if isinstance(block, (tuple, list)):
+        return make_block(int(block[0]), int(block[1]))
+    return make_block(int(block))
+
+
+def n_blocks(seq_len: int, block: BsfaBlock) -> Tuple[int, int]:
+    """(M, M_KV): query blocks ceil(N / bm) and key blocks ceil(N / bn); the last may be partial."""
+    return (-(-seq_len // block.bm) if block.bm > 0 else 0, -(-seq_len // block.bn) if block.bn > 0 else 0)
 
 
 def status_string(status: int) -> str:
@@ -147,7 +164,7 @@ def _check_all(q, k, v, out, lse, skip_counts, thresholds, shape, block, tile_st
         raise ValueError("tensors must live on the GPU")
     B, Hq, Hkv, N, d, T = (shape.batch, shape.n_heads_q, shape.n_heads_kv, shape.seq_len, shape.head_dim,
                            shape.thr_len)
-    M = -(-N // block.bm) if block.bm > 0 else 0
+    M, Mkv = n_blocks(N, block)
     _check(q, "q", torch.bfloat16, (B, Hq, N, d), dev)
     _check(k, "k", torch.bfloat16, (B, Hkv, N, d), dev)
     _check(v, "v", torch.bfloat16, (B, Hkv, N, d), dev)
@@ -155,8 +172,8 @@ def _check_all(q, k, v, out, lse, skip_counts, thresholds, shape, block, tile_st
     _check(lse, "lse", torch.float32, (B, Hq, N), dev)
     _check(skip_counts, "skip_counts", torch.int32, (B, Hq, M), dev)
     _check(thresholds, "thresholds", torch.float32, (Hq, T), dev)
-    _check(tile_state, "tile_state", torch.uint8, (B, Hq, M, M), dev)
-    _check(tile_max, "tile_max", torch.float32, (B, Hq, M, M), dev)
+    _check(tile_state, "tile_state", torch.uint8, (B, Hq, M, Mkv), dev)
+    _check(tile_max, "tile_max", torch.float32, (B, Hq, M, Mkv), dev)
 
 
 def bsfa_prefill(q, k, v, out, lse, skip_counts, thresholds, shape: BsfaShape, causal: int,
@@ -255,10 +272,10 @@ def bsfa_tile_max(q, k, tile_max, shape: BsfaShape, causal: int, block: BsfaBloc
         raise BsfaError(st, "bsfa_tile_max")
     dev = q.device
     B, Hq, Hkv, N, d = shape.batch, shape.n_heads_q, shape.n_heads_kv, shape.seq_len, shape.head_dim
-    M = -(-N // block.bm)
+    M, Mkv = n_blocks(N, block)
     _check(q, "q", torch.bfloat16, (B, Hq, N, d), dev)
     _check(k, "k", torch.bfloat16, (B, Hkv, N, d), dev)
-    _check(tile_max, "tile_max", torch.float32, (B, Hq, M, M), dev)
+    _check(tile_max, "tile_max", torch.float32, (B, Hq, M, Mkv), dev)
     st = load_library().bsfa_tile_max(_ptr(q), _ptr(k), _ptr(tile_max), shape, int(causal), block, _stream(stream))
     if st != BSFA_OK:
         raise BsfaError(st, "bsfa_tile_max")
@@ -276,13 +293,35 @@ def bsfa_calibrate_fixed_k(tile_max, n_samples: int, n_heads: int, n_blocks: int
         raise BsfaError(st, "bsfa_calibrate_fixed_k")
 
 
-def tile_max(q: torch.Tensor, k: torch.Tensor, causal: bool, block: int, stream=None) -> torch.Tensor:
-    """Allocate and fill the [B, H_q, M, M] tile maxima (``bsfa_tile_max``)."""
+def bsfa_calibrate(tile_max, shape: BsfaShape, causal: int, block: BsfaBlock, ks, thresholds,
+                   stream=None) -> None:
+    """C ABI ``bsfa_calibrate``: tile maxima [B, H_q, M, M_KV] of a ``bsfa_tile_max`` call with
+    the same shape / causal / block, ``ks`` a host sequence of ints, ``thresholds`` a
+    [len(ks), H_q, M] fp32 device tensor (see include/bsfa.h)."""
+    st = bsfa_validate(shape, causal, block)
+    if st != BSFA_OK:
+        raise BsfaError(st, "bsfa_calibrate")
+    dev = tile_max.device
+    ks = [int(x) for x in ks]
+    M, Mkv = n_blocks(shape.seq_len, block)
+    _check(tile_max, "tile_max", torch.float32, (shape.batch, shape.n_heads_q, M, Mkv), dev)
+    _check(thresholds, "thresholds", torch.float32, (len(ks), shape.n_heads_q, M), dev)
+    arr = (ctypes.c_int64 * max(len(ks), 1))(*ks)
+    st = load_library().bsfa_calibrate(_ptr(tile_max), shape, int(causal), block, ctypes.cast(arr, ctypes.c_void_p),
+                                       len(ks), _ptr(thresholds), _stream(stream))
+    if st != BSFA_OK:
+        raise BsfaError(st, "bsfa_calibrate")
+
+
+def tile_max(q: torch.Tensor, k: torch.Tensor, causal: bool, block, stream=None) -> torch.Tensor:
+    """Allocate and fill the [B, H_q, M, M_KV] tile maxima (``bsfa_tile_max``);
+    ``block`` is an int (square) or (bm, bn)."""
     B, Hq, N, d = q.shape
     shape = make_shape(B, Hq, k.shape[1], N, d, 1)
-    M = -(-N // block)  # the last block may be partial
-    out = torch.empty((B, Hq, M, M), dtype=torch.float32, device=q.device)
-    bsfa_tile_max(q, k, out, shape, int(causal), make_block(block), stream)
+    blk = as_block(block)
+    M, Mkv = n_blocks(N, blk)
+    out = torch.empty((B, Hq, M, Mkv), dtype=torch.float32, device=q.device)
+    bsfa_tile_max(q, k, out, shape, int(causal), blk, stream)
     return out
 
 
@@ -297,21 +336,33 @@ def calibrate_fixed_k(tile_maxima: torch.Tensor, k: Optional[int], causal: bool,
 
 
 def calibrate_levels(tile_maxima: torch.Tensor, ks, causal: bool, stream=None) -> torch.Tensor:
-    """Threshold tensor [len(ks), H, M]: one fixed-k table per sparsity level."""
+    """Threshold tensor [len(ks), H, M]: one fixed-k table per sparsity level (square tiles)."""
     S, H, M, _ = tile_maxima.shape
     thr = torch.empty((len(ks), H, M), dtype=torch.float32, device=tile_maxima.device)
     bsfa_calibrate_levels(tile_maxima, S, H, M, int(causal), ks, thr, stream)
     return thr
 
 
+def calibrate(tile_maxima: torch.Tensor, ks, causal: bool, block, seq_len: int, head_dim: int,
+              stream=None) -> torch.Tensor:
+    """Threshold tensor [len(ks), H, M] for any tile shape (``bsfa_calibrate``); ``tile_maxima``
+    [S, H, M, M_KV] as returned by ``tile_max`` for a sequence of ``seq_len`` positions."""
+    S, H, M, _ = tile_maxima.shape
+    blk = as_block(block)
+    shape = make_shape(S, H, 1, seq_len, head_dim, M)
+    thr = torch.empty((len(ks), H, M), dtype=torch.float32, device=tile_maxima.device)
+    bsfa_calibrate(tile_maxima, shape, int(causal), blk, ks, thr, stream)
+    return thr
+
+
 def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, thresholds: torch.Tensor, causal: bool,
-                   block: int, seq_lens: torch.Tensor, diagnostics: bool = False, stream=None) -> dict:
+                   block, seq_lens: torch.Tensor, diagnostics: bool = False, stream=None) -> dict:
     """Allocate the outputs and run ``bsfa_prefill_varlen`` (padded batch, int32 device lengths).
     Entries past each sequence are left as allocated (torch.empty)."""
     B, Hq, N, d = q.shape
     shape = make_shape(B, Hq, k.shape[1], N, d, thresholds.shape[1])
-    blk = make_block(block)
-    M = -(-N // block)
+    blk = as_block(block)
+    M, Mkv = n_blocks(N, blk)
     dev = q.device
     res = {
         "out": torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev),
@@ -319,29 +370,30 @@ def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, thresholds
         "skip_counts": torch.empty((B, Hq, M), dtype=torch.int32, device=dev),
     }
     if diagnostics:
-        res["tile_state"] = torch.empty((B, Hq, M, M), dtype=torch.uint8, device=dev)
-        res["tile_max"] = torch.empty((B, Hq, M, M), dtype=torch.float32, device=dev)
+        res["tile_state"] = torch.empty((B, Hq, M, Mkv), dtype=torch.uint8, device=dev)
+        res["tile_max"] = torch.empty((B, Hq, M, Mkv), dtype=torch.float32, device=dev)
     bsfa_prefill_varlen(q, k, v, res["out"], res["lse"], res["skip_counts"], thresholds, shape, int(causal), blk,
                         seq_lens, res.get("tile_state"), res.get("tile_max"), stream)
     return res
 
 
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, thresholds: torch.Tensor, causal: bool,
-            block: int, diagnostics: bool = False, stream=None, gate: str = "threshold",
+            block, diagnostics: bool = False, stream=None, gate: str = "threshold",
             out_dtype: torch.dtype = torch.float32) -> dict:
     """Allocate the outputs and run the forward pass.
 
     ``bsfa_prefill`` by default; ``bsfa_prefill_ex`` with diagnostics;
     ``bsfa_prefill_gated`` for ``gate="gap"``; ``bsfa_prefill_bf16`` for a
     bf16 output (threshold gate, no diagnostics).
-    q: bf16 [B, H_q, N, d]; k, v: bf16 [B, H_kv, N, d]; thresholds: fp32 [H_q, T_len].
+    q: bf16 [B, H_q, N, d]; k, v: bf16 [B, H_kv, N, d]; thresholds: fp32 [H_q, T_len];
+    block: an int (square tile) or (bm, bn).
     Returns a dict of device tensors: out, lse, skip_counts (+ tile_state, tile_max).
     """
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
     shape = make_shape(B, Hq, Hkv, N, d, thresholds.shape[1])
-    blk = make_block(block)
-    M = -(-N // block)  # the last block may be partial
+    blk = as_block(block)
+    M, Mkv = n_blocks(N, blk)
     dev = q.device
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("out_dtype must be float32 or bfloat16")
@@ -360,14 +412,14 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, thresholds: torch
         return res
     if gate != "threshold":
         if diagnostics:
-            res["tile_state"] = torch.empty((B, Hq, M, M), dtype=torch.uint8, device=dev)
-            res["tile_max"] = torch.empty((B, Hq, M, M), dtype=torch.float32, device=dev)
+            res["tile_state"] = torch.empty((B, Hq, M, Mkv), dtype=torch.uint8, device=dev)
+            res["tile_max"] = torch.empty((B, Hq, M, Mkv), dtype=torch.float32, device=dev)
         bsfa_prefill_gated(q, k, v, res["out"], res["lse"], res["skip_counts"], thresholds, shape, int(causal),
                            blk, GATES[gate], res.get("tile_state"), res.get("tile_max"), stream)
         return res
     if diagnostics:
-        res["tile_state"] = torch.empty((B, Hq, M, M), dtype=torch.uint8, device=dev)
-        res["tile_max"] = torch.empty((B, Hq, M, M), dtype=torch.float32, device=dev)
+        res["tile_state"] = torch.empty((B, Hq, M, Mkv), dtype=torch.uint8, device=dev)
+        res["tile_max"] = torch.empty((B, Hq, M, Mkv), dtype=torch.float32, device=dev)
         bsfa_prefill_ex(q, k, v, res["out"], res["lse"], res["skip_counts"], thresholds, shape, int(causal), blk,
                         res["tile_state"], res["tile_max"], stream)
     else:

@@ -18,12 +18,11 @@ int check_shape(const bsfa_shape& s, int causal, const bsfa_block& blk) {
   if (causal != 0 && causal != 1) return BSFA_ERR_SHAPE;
   if (s.n_heads_q % s.n_heads_kv) return BSFA_ERR_SHAPE;
   if (blk.bm < 1 || blk.bn < 1) return BSFA_ERR_SHAPE;
-  if (blk.bm != blk.bn) return BSFA_ERR_UNSUPPORTED;
-  if (blk.bm != 64 && blk.bm != 128) return BSFA_ERR_UNSUPPORTED;
+  if ((blk.bm != 64 && blk.bm != 128) || (blk.bn != 64 && blk.bn != 128)) return BSFA_ERR_UNSUPPORTED;
   if (s.head_dim != 64 && s.head_dim != 128) return BSFA_ERR_UNSUPPORTED;
   // the kernels index heads, rows and thresholds with 32-bit integers
   const int64_t lim = INT32_MAX;
-  const int64_t m = (s.seq_len + blk.bm - 1) / blk.bm;  // the last block may be partial
+  const int64_t m = (s.seq_len + blk.bm - 1) / blk.bm;  // query blocks; the last may be partial
   if (s.seq_len > lim / 2 || s.batch > lim || s.n_heads_q > lim) return BSFA_ERR_SHAPE;
   if (s.batch * s.n_heads_q > lim / m) return BSFA_ERR_SHAPE;    // workgroups
   if (s.n_heads_q > lim / s.thr_len) return BSFA_ERR_SHAPE;      // threshold index
@@ -39,6 +38,7 @@ bsfa::FwdParams shape_params(const bsfa_shape& shape, const bsfa_block& block) {
   p.G = p.Hq / p.Hkv;
   p.N = (int)shape.seq_len;
   p.M = (int)((shape.seq_len + block.bm - 1) / block.bm);
+  p.Mkv = (int)((shape.seq_len + block.bn - 1) / block.bn);
   p.T_len = (int)shape.thr_len;
   p.scale = (float)(1.0 / sqrt((double)shape.head_dim));
   p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)shape.head_dim));
@@ -75,8 +75,32 @@ int prefill_impl(const void* q, const void* k, const void* v, float* out, uint16
   p.tile_state = tile_state;
   p.tile_max = tile_max;
   p.seq_lens = seq_lens;
-  return bsfa::launch_fwd(p, (int)shape.head_dim, block.bm, causal, diagnostics,
+  return bsfa::launch_fwd(p, (int)shape.head_dim, block.bm, block.bn, causal, diagnostics,
                           static_cast<hipStream_t>(stream));
+}
+
+// One launch per level; ks clamped to the number of key blocks (k >= n_i
+// means "keep all" for every query block alike).
+int calibrate_impl(const float* tile_max, int64_t n_samples, int64_t n_heads, int64_t mq, int64_t mkv,
+                          int bm, int bn, int causal, const int64_t* ks, int64_t n_levels, float* thresholds,
+                          void* stream) {
+  if (n_samples < 1 || n_heads < 1 || mq < 1 || mkv < 1 || n_levels < 1 || (causal != 0 && causal != 1))
+    return BSFA_ERR_SHAPE;
+  if (!ks || !tile_max || !thresholds) return BSFA_ERR_NULL;
+  for (int64_t l = 0; l < n_levels; ++l)
+    if (ks[l] < 0) return BSFA_ERR_SHAPE;
+  if (mkv > bsfa::kCalibMaxBlocks) return BSFA_ERR_UNSUPPORTED;
+  if (n_heads > INT32_MAX / mq || n_samples > INT32_MAX || n_levels > INT32_MAX / (n_heads * mq))
+    return BSFA_ERR_SHAPE;
+  if (!aligned(tile_max, 4) || !aligned(thresholds, 4)) return BSFA_ERR_ALIGN;
+  const int64_t level_size = n_heads * mq;
+  for (int64_t l = 0; l < n_levels; ++l) {
+    const int kk = (int)(ks[l] < mkv ? ks[l] : mkv);
+    const int st = bsfa::launch_calibrate(tile_max, (int)n_samples, (int)n_heads, (int)mq, (int)mkv, bm, bn, causal,
+                                          kk, thresholds + l * level_size, static_cast<hipStream_t>(stream));
+    if (st != BSFA_OK) return st;
+  }
+  return BSFA_OK;
 }
 
 }  // namespace
@@ -143,41 +167,30 @@ int bsfa_tile_max(const void* q, const void* k, float* tile_max, bsfa_shape shap
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
   p.tile_max = tile_max;
-  return bsfa::launch_fwd(p, (int)shape.head_dim, block.bm, causal, 2, static_cast<hipStream_t>(stream));
+  return bsfa::launch_fwd(p, (int)shape.head_dim, block.bm, block.bn, causal, 2, static_cast<hipStream_t>(stream));
 }
 
 int bsfa_calibrate_fixed_k(const float* tile_max, int64_t n_samples, int64_t n_heads, int64_t n_blocks, int causal,
                            int64_t k, float* thresholds, void* stream) {
-  if (n_samples < 1 || n_heads < 1 || n_blocks < 1 || k < 0 || (causal != 0 && causal != 1))
-    return BSFA_ERR_SHAPE;
-  if (n_blocks > bsfa::kCalibMaxBlocks) return BSFA_ERR_UNSUPPORTED;
-  if (n_heads * n_blocks > INT32_MAX || n_samples > INT32_MAX) return BSFA_ERR_SHAPE;
-  if (!tile_max || !thresholds) return BSFA_ERR_NULL;
-  if (!aligned(tile_max, 4) || !aligned(thresholds, 4)) return BSFA_ERR_ALIGN;
-  const int kk = (int)(k < n_blocks ? k : n_blocks);
-  return bsfa::launch_calibrate(tile_max, (int)n_samples, (int)n_heads, (int)n_blocks, causal, kk, thresholds,
-                                static_cast<hipStream_t>(stream));
+  if (k < 0) return BSFA_ERR_SHAPE;
+  // square tiles: the diagonal of query block i is key block i, whatever the size
+  return calibrate_impl(tile_max, n_samples, n_heads, n_blocks, n_blocks, 1, 1, causal, &k, 1, thresholds, stream);
 }
 
 int bsfa_calibrate_levels(const float* tile_max, int64_t n_samples, int64_t n_heads, int64_t n_blocks, int causal,
                           const int64_t* ks, int64_t n_levels, float* thresholds, void* stream) {
-  if (n_samples < 1 || n_heads < 1 || n_blocks < 1 || n_levels < 1 || (causal != 0 && causal != 1))
-    return BSFA_ERR_SHAPE;
-  if (!ks || !tile_max || !thresholds) return BSFA_ERR_NULL;
-  for (int64_t l = 0; l < n_levels; ++l)
-    if (ks[l] < 0) return BSFA_ERR_SHAPE;
-  if (n_blocks > bsfa::kCalibMaxBlocks) return BSFA_ERR_UNSUPPORTED;
-  if (n_heads * n_blocks > INT32_MAX || n_samples > INT32_MAX || n_levels > INT32_MAX / (n_heads * n_blocks))
-    return BSFA_ERR_SHAPE;
-  if (!aligned(tile_max, 4) || !aligned(thresholds, 4)) return BSFA_ERR_ALIGN;
-  const int64_t level_size = n_heads * n_blocks;
-  for (int64_t l = 0; l < n_levels; ++l) {
-    const int kk = (int)(ks[l] < n_blocks ? ks[l] : n_blocks);
-    const int st = bsfa::launch_calibrate(tile_max, (int)n_samples, (int)n_heads, (int)n_blocks, causal, kk,
-                                          thresholds + l * level_size, static_cast<hipStream_t>(stream));
-    if (st != BSFA_OK) return st;
-  }
-  return BSFA_OK;
+  return calibrate_impl(tile_max, n_samples, n_heads, n_blocks, n_blocks, 1, 1, causal, ks, n_levels, thresholds,
+                        stream);
+}
+
+int bsfa_calibrate(const float* tile_max, bsfa_shape shape, int causal, bsfa_block block, const int64_t* ks,
+                   int64_t n_levels, float* thresholds, void* stream) {
+  const int st = check_shape(shape, causal, block);
+  if (st != BSFA_OK) return st;
+  const int64_t mq = (shape.seq_len + block.bm - 1) / block.bm;
+  const int64_t mkv = (shape.seq_len + block.bn - 1) / block.bn;
+  return calibrate_impl(tile_max, shape.batch, shape.n_heads_q, mq, mkv, block.bm, block.bn, causal, ks, n_levels,
+                        thresholds, stream);
 }
 
 }  // extern "C"

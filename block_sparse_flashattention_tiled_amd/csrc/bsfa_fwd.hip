@@ -1,820 +1,15 @@
-// Block-sparse FlashAttention prefill forward kernel for gfx950 (MI355X).
-//
-// Operation: "Block Sparse Flash Attention" (paperpeel.com/paper/2512.07011).
-// FlashAttention-2's tiled online softmax (App. B.2 steps (1)-(6)) with one
-// gate per score tile (Sec. 4.1, 4.4): after S_ij = Q_i K_j^T / sqrt(d) is
-// formed, its maximum over visible entries is compared with the threshold of
-// (head, query block); an off-diagonal tile below it is skipped before any of
-// its V rows is requested, and contributes nothing to the running max, sum
-// or output.  Diagonal tiles always pass (Sec. 4.1); causal tiles above the
-// diagonal are never visited (App. B.2).
-//
-// Mapping onto CDNA4:
-//  * one workgroup per (batch, query head, query block); BLK/32 waves, wave w
-//    owns query rows [32w, 32w+32) of the block.  The kernel is sized to run
-//    two workgroups per CU (LDS < 80 KB, <= 256 registers per lane) so that
-//    one workgroup's MFMA phases overlap the other's softmax and waits;
-//  * both contractions run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
-//    Scores are formed transposed, S^T = K Q^T, so that each lane ends up
-//    holding one query row: its row statistics stay in-lane and the score
-//    registers, exponentiated and rounded to bf16, are directly the B operand
-//    of O^T = V^T P^T (both operands use the same k-slot order);
-//  * Q lives in registers for the whole key loop (B.2 step (1));
-//  * K_{j+1} is requested into registers before S_j is computed and written
-//    to the (row-padded) K tile in LDS once every wave is done with K_j;
-//  * V_j is requested only after tile j passed its gate; its loads overlap
-//    the softmax of the tile, then it is written to LDS.  The A operand of
-//    O^T = V^T P^T needs V transposed: it is read with ds_read_b64_tr_b16,
-//    whose 16-lane groups return a 4x16 block transposed.  The V tile is
-//    XOR-swizzled so those reads are bank-conflict free;
-//  * the tile maximum is reduced in-lane, across the wave with shuffles and
-//    across waves through LDS; the skip decision is read back into a scalar
-//    register so the branch is uniform for the workgroup;
-//  * the running output is rescaled lazily: only when a row maximum grows by
-//    more than 2^4 (exact: O and l always refer to the same reference max),
-//    and l sums the bf16-rounded P~ that multiplies V;
-//  * barriers fence LDS only, so outstanding global loads stay in flight;
-//  * workgroups are ordered heaviest query block first (causal) and, when the
-//    grid allows, remapped so that the query heads of one KV group run back
-//    to back on the same XCD and share K_j/V_j in that XCD's L2.
-#include <hip/hip_runtime.h>
-#include <math.h>
-#include <stdint.h>
-
-#include <type_traits>
-
+// Dispatch of the forward kernels by tile shape.  The kernels themselves are
+// in bsfa_fwd_kernels.h, instantiated once per tile shape in
+// bsfa_fwd_<bm>x<bn>.hip so that the shapes compile in parallel.
 #include "bsfa_internal.h"
 
 namespace bsfa {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-template <int D, int BLK>
-struct Cfg {
-  static constexpr int NW = BLK / 32;        // waves per workgroup
-  static constexpr int NT = NW * 64;         // threads per workgroup
-  static constexpr int KC = D / 16;          // 16-wide d chunks of the QK^T contraction
-  static constexpr int KB = BLK / 32;        // 32-key sub-blocks of a tile
-  static constexpr int PC = BLK / 16;        // 16-key chunks of the P.V contraction
-  static constexpr int DB = D / 32;          // 32-wide d sub-blocks of the output
-  static constexpr int CPR = D / 8;          // 16-byte chunks per K / V row
-  static constexpr int LD = D / 16;          // 16-byte chunks per thread per tile
-  static constexpr int KS = D * 2 + 16;      // K row stride in LDS (bytes): b128 reads conflict free
-  static constexpr int K_BYTES = BLK * KS;
-  static constexpr int V_BYTES = BLK * D * 2;  // dense, XOR-swizzled
-  static constexpr int LDS_BYTES = K_BYTES + V_BYTES + 16 * NW;
-};
-
-// 16-byte chunk position of logical chunk cc of V row `row`: XOR with a
-// function of the row so that the transposing reads (4 rows x 4 chunks per
-// 32 lanes) hit 64 distinct banks.
-template <int D>
-__device__ __forceinline__ int v_swz(int row) {
-  return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
-}
-
-// Workgroup barrier that orders LDS accesses only: global loads issued before
-// it stay in flight.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// Gate of one query unit for tile j (a5).  Threshold gate (the pages'
-// method, "Block Sparse Flash Attention" Sec. 4.1 and 4.4): an off-diagonal
-// tile is skipped iff s_max < tau, strictly.  Gap gate (the comparison
-// reference of BLASST and of SpargeAttention's in-kernel P.V skip, Sec. 3
-// "Related Work": a tile far below the running maximum): skipped iff
-// s_max < M - tau, where M is the largest s_max among the unit's tiles kept so
-// far.  Both compare in the scaled-score domain; NaN compares false (kept).
-__device__ __forceinline__ int gate_skip(int gap, bool off_diag, float tms, float tau, float& mrun) {
-  const float ref = gap ? mrun - tau : tau;
-  const int skip = (off_diag && tms < ref) ? 1 : 0;
-  if (!skip) mrun = fmaxf(mrun, tms);
-  return skip;
-}
-
-// (a9) one lane's share of an output row O = O_acc / l: four runs of four
-// consecutive columns per 32-column block, fp32, or rounded to bf16 (nearest
-// even) when the caller asked for a bf16 output.
-template <int DB>
-__device__ __forceinline__ void store_out_row(const FwdParams& p, size_t row, const f32x16 (&o)[DB], float inv,
-                                              int hh) {
-  constexpr int D = DB * 32;
-  if (p.out_bf16) {
-    uint16_t* ob = p.out_bf16 + row * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x2 lo = {o[db][4 * g4 + 0] * inv, o[db][4 * g4 + 1] * inv};
-        const f32x2 hi = {o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv};
-        uint2 val;
-        val.x = __builtin_bit_cast(unsigned, __builtin_convertvector(lo, bf16x2));
-        val.y = __builtin_bit_cast(unsigned, __builtin_convertvector(hi, bf16x2));
-        *reinterpret_cast<uint2*>(ob + db * 32 + 8 * g4 + 4 * hh) = val;
-      }
-    return;
-  }
-  float* og = p.out + row * D;
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      float4 val;
-      val.x = o[db][4 * g4 + 0] * inv;
-      val.y = o[db][4 * g4 + 1] * inv;
-      val.z = o[db][4 * g4 + 2] * inv;
-      val.w = o[db][4 * g4 + 3] * inv;
-      *reinterpret_cast<float4*>(og + db * 32 + 8 * g4 + 4 * hh) = val;
-    }
-}
-
-// Sequences whose length N is not a multiple of the tile: the last query and
-// key blocks are partial, and positions >= N do not exist (masked, not padded).
-// tile_chunk: index of 16-byte chunk c of the tile whose first row is r0, with
-// rows past the end reading the last row instead, so that every load stays
-// inside the tensor; mask_tail sets the scores of query rows >= rows_left and of
-// keys >= keys_left (both relative to the tile) to -inf, so the values read
-// there never reach a maximum, a sum or an output.
-template <int CPR>
-__device__ __forceinline__ size_t tile_chunk(int r0, int c, int n) {
-  const int row = min(r0 + c / CPR, n - 1);
-  return (size_t)row * CPR + c % CPR;
-}
-template <int NKB>
-__device__ __forceinline__ void mask_tail(f32x16 (&s)[NKB], int qloc, int hh, int rows_left, int keys_left) {
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      if (qloc >= rows_left || key >= keys_left) s[kb][r] = -INFINITY;
-    }
-}
-
-// S^T = K_j Q_i^T for this wave's 32 query rows.
-// s[kb][r] = raw score of query row (lane % 32) and key kb*32 + 8(r/4) + 4(lane/32) + r%4.
-template <int D, int BLK, int NKB, int NKC>
-__device__ __forceinline__ void qk_tile(f32x16 (&s)[NKB], const char* ks, int k_lane, const bf16x8 (&qf)[NKC]) {
-  using C = Cfg<D, BLK>;
-  static_assert(NKB == C::KB && NKC == C::KC, "fragment sizes");
-#pragma unroll
-  for (int kb = 0; kb < C::KB; ++kb) s[kb] = f32x16{};
-  // d-chunk outer, key block inner: consecutive MFMAs use independent
-  // accumulators and the next chunk's K fragments load while they run
-#pragma unroll
-  for (int c = 0; c < C::KC; ++c) {
-    bf16x8 a[C::KB];
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-      a[kb] = *reinterpret_cast<const bf16x8*>(ks + k_lane + kb * 32 * C::KS + c * 32);
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], qf[c], s[kb], 0, 0, 0);
-  }
-}
-
-// MAXONLY: calibration pass - only the tile maxima of every computed tile are
-// produced (no gate, no V, no output); used to build threshold tables.
-template <int D, int BLK, bool CAUSAL, bool DIAG_OUT, bool MAXONLY, bool RAGGED>
-__global__ void __launch_bounds__(BLK * 2) bsfa_fwd_kernel(const FwdParams p) {
-  using C = Cfg<D, BLK>;
-  __shared__ __attribute__((aligned(16))) char v_lds[C::V_BYTES];
-  __shared__ __attribute__((aligned(16))) char k_lds[C::K_BYTES];
-  __shared__ float red[C::NW];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;
-
-  // ---- work item (a1): workgroup -> (b, query head, query block) ----------
-  int L = blockIdx.x;
-  if (p.remap) {
-    // consecutive workgroups go to consecutive XCDs; regroup so that one XCD
-    // runs the G query heads of a KV group on the same query block together
-    const int x = L & 7;
-    const int pp = L >> 3;
-    L = ((pp / p.G) * 8 + x) * p.G + (pp % p.G);
-  }
-  const int hin = L % p.G;
-  L /= p.G;
-  const int g = L % p.Hkv;
-  L /= p.Hkv;
-  const int b = L % p.B;
-  L /= p.B;
-  const int i = CAUSAL ? (p.M - 1 - L) : L;  // causal: heaviest query blocks first
-  const int hq = g * p.G + hin;
-  // length of this batch element's sequence (per-sequence lengths: clamped to
-  // [0, N]); a query block past its end has nothing to compute or write
-  const int n_seq = (RAGGED && p.seq_lens) ? min(max(p.seq_lens[b], 0), p.N) : p.N;
-  const int m_seq = RAGGED ? (n_seq + BLK - 1) / BLK : p.M;
-  if (RAGGED && i >= m_seq) return;
-
-  const size_t q_head = (size_t)(b * p.Hq + hq) * p.N;
-  const size_t kv_head = (size_t)(b * p.Hkv + g) * p.N;
-  const int qloc = 32 * w + l32;  // this lane's query row inside the block
-  const int qrow = i * BLK + qloc;
-  constexpr int TILE_CHUNKS = BLK * D / 8;  // 16-byte chunks per K or V tile
-
-  // per-lane LDS byte offset of the K operand reads
-  const int k_lane = l32 * C::KS + hh * 16;
-  // ds_read_b64_tr_b16: source lane 4e + c of each 16-lane group points at
-  // V[key0 + e][d0 + 4c]; lane j of the group then receives V[key0..key0+3][d0 + j]
-  const int v_e = (lane & 15) >> 2;
-  const int v_row = 4 * hh + v_e;                       // + 16 kc + 8 half
-  const int v_col = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // 16-byte chunk, + 4 db
-  const int v_half = (lane & 1) * 8;
-  const u32x4* vg = reinterpret_cast<const u32x4*>(p.v) + kv_head * C::CPR;
-
-  // ---- (a2) Q_i stays in registers: B operand of S^T = K Q^T --------------
-  bf16x8 qf[C::KC];
-  {
-    const u32x4* qg = reinterpret_cast<const u32x4*>(p.q) + (q_head + (RAGGED ? min(qrow, n_seq - 1) : qrow)) * C::CPR;
-#pragma unroll
-    for (int c = 0; c < C::KC; ++c) qf[c] = __builtin_bit_cast(bf16x8, qg[2 * c + hh]);
-  }
-  const u32x4* kg = reinterpret_cast<const u32x4*>(p.k) + kv_head * C::CPR;
-
-  // threshold of (head, query block); blocks past the table reuse the last entry
-  const float tau = MAXONLY ? INFINITY : p.thresholds[hq * p.T_len + min(i, p.T_len - 1)];
-  const float c2 = p.scale_log2;
-  const int jend = CAUSAL ? i : m_seq - 1;
-  const size_t diag_row = ((size_t)(b * p.Hq + hq) * p.M + i) * p.M;
-
-  f32x16 o[C::DB];
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db) o[db] = f32x16{};
-  float m_run = -INFINITY;  // reference max of O and l, in units of scale*log2(e)
-  float l_run = 0.f;        // sum of exp over this lane's half of the keys (for lse)
-  float lb_run = 0.f;       // the same sum over the bf16-rounded P~ (normalises O)
-  float mrun = -INFINITY;   // largest s_max of the kept tiles (gap gate)
-  int nskip = 0;
-
-  // K_0 -> LDS
-  u32x4 kreg[C::LD];
-  u32x4 vreg[C::LD];
-#pragma unroll
-  for (int it = 0; it < C::LD; ++it) {
-    const int c = tid + C::NT * it;
-    kreg[it] = kg[RAGGED ? tile_chunk<C::CPR>(0, c, n_seq) : c];
-  }
-#pragma unroll
-  for (int it = 0; it < C::LD; ++it) {
-    const int c = tid + C::NT * it;
-    *reinterpret_cast<u32x4*>(k_lds + (c / C::CPR) * C::KS + (c % C::CPR) * 16) = kreg[it];
-  }
-
-  for (int j = 0; j <= jend; ++j) {
-    lds_barrier();  // (a): K_j visible; every wave is done with V_{j-1}
-    // ---- (a3) request K_{j+1} into registers (skipped tiles included) -----
-    const bool more = j < jend;
-    if (more) {
-      const u32x4* src = kg + (size_t)(j + 1) * TILE_CHUNKS;
-#pragma unroll
-      for (int it = 0; it < C::LD; ++it) {
-        const int c = tid + C::NT * it;
-        kreg[it] = RAGGED ? kg[tile_chunk<C::CPR>((j + 1) * BLK, c, n_seq)] : src[c];
-      }
-    }
-    // ---- (a4) S^T = K_j Q_i^T on MFMA --------------------------------------
-    f32x16 s[C::KB];
-    qk_tile<D, BLK>(s, k_lds, k_lane, qf);
-    const bool diag = (j == i);
-    if (CAUSAL && diag) {
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key > qloc) s[kb][r] = -INFINITY;
-        }
-    }
-    if (RAGGED) {
-      const int rows_left = n_seq - i * BLK, keys_left = n_seq - j * BLK;
-      if (rows_left < BLK || keys_left < BLK) mask_tail(s, qloc, hh, rows_left, keys_left);
-    }
-    // ---- (a5) tile maximum and gate ---------------------------------------
-    float rm0 = -INFINITY, rm1 = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        rm0 = fmaxf(rm0, s[kb][r]);
-        rm1 = fmaxf(rm1, s[kb][r + 1]);
-      }
-    float rm = fmaxf(rm0, rm1);
-    rm = fmaxf(rm, __shfl_xor(rm, 32));  // full row max of query qloc
-    float wm = rm;
-#pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) wm = fmaxf(wm, __shfl_xor(wm, off));
-    if (lane == 0) red[w] = wm;
-    lds_barrier();  // (b): every wave is done with K_j; red complete
-    float tm = red[0];
-#pragma unroll
-    for (int ww = 1; ww < C::NW; ++ww) tm = fmaxf(tm, red[ww]);
-    const float tms = tm * p.scale;  // s_max in the scaled-score domain
-    int skip = MAXONLY ? 1 : gate_skip(p.gate, !diag, tms, tau, mrun);
-    skip = __builtin_amdgcn_readfirstlane(skip);
-    if (DIAG_OUT && tid == 0) {
-      if (p.tile_state) p.tile_state[diag_row + j] = diag ? 3 : (skip ? 2 : 1);
-      if (p.tile_max) p.tile_max[diag_row + j] = tms;
-    }
-    // ---- (a8) V_j requested only for a kept tile ---------------------------
-    if (!skip) {
-      const u32x4* src = vg + (size_t)j * TILE_CHUNKS;
-#pragma unroll
-      for (int it = 0; it < C::LD; ++it) {
-        const int c = tid + C::NT * it;
-        vreg[it] = RAGGED ? vg[tile_chunk<C::CPR>(j * BLK, c, n_seq)] : src[c];
-      }
-    }
-    // K_{j+1} -> LDS (every wave has finished reading K_j)
-    if (more) {
-#pragma unroll
-      for (int it = 0; it < C::LD; ++it) {
-        const int c = tid + C::NT * it;
-        *reinterpret_cast<u32x4*>(k_lds + (c / C::CPR) * C::KS + (c % C::CPR) * 16) = kreg[it];
-      }
-    }
-    if (skip) {  // (a6): no V load, no exp, no statistics update
-      ++nskip;
-      continue;
-    }
-
-    // ---- (a7) online softmax while V_j is in flight --------------------------
-    // O and l refer to the reference max m_run; it is raised (and O, l
-    // rescaled) only when a row maximum exceeds it by more than 2^4, so
-    // P~ <= 16.  The output is normalised by the sum of the same bf16-rounded
-    // P~ that multiplies V, so the weights of a row normalise exactly; lse
-    // uses the fp32 sum.
-    const float m_tile = rm * c2;
-    const bool grow = m_tile > m_run + 4.f;
-    if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform: rescale O and l
-      const float m_new = grow ? m_tile : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-      lb_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
-      m_run = m_new;
-    }
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    float rs0 = 0.f, rs1 = 0.f, rb0 = 0.f, rb1 = 0.f;
-    bf16x8 pf[C::PC];
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int r = 0; r < 8; r += 2) {
-          f32x2 pr;
-          pr[0] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hf + r], c2, -m_run));
-          pr[1] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hf + r + 1], c2, -m_run));
-          const bf16x2 pb = __builtin_convertvector(pr, bf16x2);
-          rs0 += pr[0];
-          rs1 += pr[1];
-          if (r & 2) rb1 = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, rb1, false);
-          else rb0 = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, rb0, false);
-          pf[2 * kb + hf][r] = pb[0];
-          pf[2 * kb + hf][r + 1] = pb[1];
-        }
-    l_run += rs0 + rs1;
-    lb_run += rb0 + rb1;
-
-    // V_j -> LDS (swizzled rows); its loads overlapped the softmax
-#pragma unroll
-    for (int it = 0; it < C::LD; ++it) {
-      const int c = tid + C::NT * it;
-      const int row = c / C::CPR;
-      *reinterpret_cast<u32x4*>(v_lds + row * (2 * D) + ((c % C::CPR) ^ v_swz<D>(row)) * 16) = vreg[it];
-    }
-    lds_barrier();  // (c): V_j complete
-    // ---- (a8) O^T += V_j^T P~^T on MFMA -----------------------------------
-#pragma unroll
-    for (int kc = 0; kc < C::PC; ++kc)
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        const int row = 16 * kc + v_row;
-        const int chunk = (4 * db + v_col) ^ v_swz<D>(row);
-        const char* base = v_lds + row * (2 * D) + chunk * 16 + v_half;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * 2 * D));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kc], o[db], 0, 0, 0);
-      }
-  }
-
-  if (MAXONLY) {
-    if (CAUSAL || RAGGED)
-      for (int jj = jend + 1 + tid; jj < p.M; jj += C::NT) p.tile_max[diag_row + jj] = __builtin_nanf("");
-    return;
-  }
-  // ---- (a9) epilogue: O_i = O_acc / l, lse, skip count -------------------
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.f / (lb_run + __shfl_xor(lb_run, 32));
-  if (!RAGGED || qrow < n_seq) {
-    store_out_row(p, q_head + qrow, o, inv, hh);
-    if (p.lse && hh == 0) p.lse[q_head + qrow] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
-  }
-  if (p.skip_counts && tid == 0) p.skip_counts[(size_t)(b * p.Hq + hq) * p.M + i] = nskip;
-  if (DIAG_OUT && (CAUSAL || RAGGED)) {
-    for (int jj = jend + 1 + tid; jj < p.M; jj += C::NT) {
-      if (p.tile_state) p.tile_state[diag_row + jj] = 0;
-      if (p.tile_max) p.tile_max[diag_row + jj] = __builtin_nanf("");
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Paired variant: one workgroup of 2*BLK/32 waves runs two query units that
-// read the same K/V stream - two query heads of one KV group on the same query
-// block, or (bidirectional) two neighbouring query blocks of one head.  Q of
-// both units sits in LDS, so a wave needs no Q registers and two waves fit on
-// each SIMD; K_j is loaded once for both units.  Each unit keeps its own gate,
-// statistics and output; V_j is requested when at least one unit keeps tile j
-// and a unit that skipped the tile neither reads it nor updates anything.
-// ---------------------------------------------------------------------------
-template <int D, int BLK>
-struct PairCfg {
-  using C = Cfg<D, BLK>;
-  static constexpr int NWU = BLK / 32;              // waves per unit
-  static constexpr int NW = 2 * NWU;                // waves per workgroup
-  static constexpr int NT = NW * 64;                // threads per workgroup
-  static constexpr int LD = BLK * D / 8 / NT;       // 16-byte chunks per thread per K / V tile
-  static constexpr int Q_BYTES = BLK * C::KS;       // Q tile, rows padded like K
-};
-
-// S^T = K_j Q^T with the Q fragments read from LDS.
-template <int D, int BLK, int NKB>
-__device__ __forceinline__ void qk_tile_qlds(f32x16 (&s)[NKB], const char* ks, int k_lane, const char* qs,
-                                             int q_lane) {
-  using C = Cfg<D, BLK>;
-  static_assert(NKB == C::KB, "fragment size");
-#pragma unroll
-  for (int kb = 0; kb < C::KB; ++kb) s[kb] = f32x16{};
-#pragma unroll
-  for (int c = 0; c < C::KC; ++c) {
-    const bf16x8 qb = *reinterpret_cast<const bf16x8*>(qs + q_lane + c * 32);
-    bf16x8 a[C::KB];
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-      a[kb] = *reinterpret_cast<const bf16x8*>(ks + k_lane + kb * 32 * C::KS + c * 32);
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], qb, s[kb], 0, 0, 0);
-  }
-}
-
-// HEADPAIR: units are query heads 2hp, 2hp+1 of a KV group (same query block);
-// otherwise (bidirectional only) query blocks 2ip, 2ip+1 of one head.
-template <int D, int BLK, bool CAUSAL, bool DIAG_OUT, bool MAXONLY, bool HEADPAIR, bool RAGGED>
-__global__ void __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2, 2)))
-    bsfa_fwd_pair_kernel(const FwdParams p) {
-  using C = Cfg<D, BLK>;
-  using P2 = PairCfg<D, BLK>;
-  static_assert(HEADPAIR || !CAUSAL, "block pairs are for bidirectional attention");
-  __shared__ __attribute__((aligned(16))) char q_lds[2][P2::Q_BYTES];
-  __shared__ __attribute__((aligned(16))) char k_lds[C::K_BYTES];
-  __shared__ __attribute__((aligned(16))) char v_lds[C::V_BYTES];
-  __shared__ float red[2][P2::NWU];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int u = w / P2::NWU;   // unit of this wave
-  const int wu = w % P2::NWU;  // wave inside the unit
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;
-
-  // ---- work item (a1): workgroup -> (b, KV group, two units) --------------
-  const int per_group = HEADPAIR ? p.G / 2 : p.G;  // workgroups per KV group and block (pair)
-  int L = blockIdx.x;
-  if (p.remap) {
-    const int x = L & 7;
-    const int pp = L >> 3;
-    L = ((pp / per_group) * 8 + x) * per_group + (pp % per_group);
-  }
-  const int hin = L % per_group;
-  L /= per_group;
-  const int g = L % p.Hkv;
-  L /= p.Hkv;
-  const int b = L % p.B;
-  L /= p.B;
-  int hq_u[2], i_u[2];
-  if (HEADPAIR) {
-    const int i = CAUSAL ? (p.M - 1 - L) : L;  // causal: heaviest query blocks first
-    hq_u[0] = g * p.G + 2 * hin;
-    hq_u[1] = hq_u[0] + 1;
-    i_u[0] = i_u[1] = i;
-  } else {
-    hq_u[0] = hq_u[1] = g * p.G + hin;
-    i_u[0] = 2 * L;
-    i_u[1] = 2 * L + 1;
-  }
-  const int hq = hq_u[u];
-  const int i = i_u[u];
-  // per-sequence length (see the one-unit kernel).  A block pair whose second
-  // block lies past the end keeps that unit running through the barriers; it
-  // writes nothing
-  const int n_seq = (RAGGED && p.seq_lens) ? min(max(p.seq_lens[b], 0), p.N) : p.N;
-  const int m_seq = RAGGED ? (n_seq + BLK - 1) / BLK : p.M;
-  if (RAGGED && i_u[0] >= m_seq) return;  // both units past the end (i_u[0] <= i_u[1])
-  const bool live = !RAGGED || i < m_seq;
-  const size_t q_head = (size_t)(b * p.Hq + hq) * p.N;
-  const size_t kv_head = (size_t)(b * p.Hkv + g) * p.N;
-  const int qloc = 32 * wu + l32;
-  const int qrow = i * BLK + qloc;
-  constexpr int TILE_CHUNKS = BLK * D / 8;
-
-  const int k_lane = l32 * C::KS + hh * 16;
-  const int q_lane = qloc * C::KS + hh * 16;
-  const int v_row = 4 * hh + ((lane & 15) >> 2);
-  const int v_col = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  const int v_half = (lane & 1) * 8;
-
-  // ---- (a2) Q of both units -> LDS ------------------------------------------
-#pragma unroll
-  for (int uu = 0; uu < 2; ++uu) {
-    const u32x4* qh = reinterpret_cast<const u32x4*>(p.q) + (size_t)(b * p.Hq + hq_u[uu]) * p.N * C::CPR;
-    const u32x4* qg = qh + (size_t)i_u[uu] * BLK * C::CPR;
-    u32x4 qr[P2::LD];
-#pragma unroll
-    for (int it = 0; it < P2::LD; ++it) {
-      const int c = tid + P2::NT * it;
-      qr[it] = RAGGED ? qh[tile_chunk<C::CPR>(i_u[uu] * BLK, c, n_seq)] : qg[c];
-    }
-#pragma unroll
-    for (int it = 0; it < P2::LD; ++it) {
-      const int c = tid + P2::NT * it;
-      *reinterpret_cast<u32x4*>(q_lds[uu] + (c / C::CPR) * C::KS + (c % C::CPR) * 16) = qr[it];
-    }
-  }
-  const u32x4* kg = reinterpret_cast<const u32x4*>(p.k) + kv_head * C::CPR;
-  const u32x4* vg = reinterpret_cast<const u32x4*>(p.v) + kv_head * C::CPR;
-
-  float tau_u[2];
-#pragma unroll
-  for (int uu = 0; uu < 2; ++uu)
-    tau_u[uu] = MAXONLY ? INFINITY : p.thresholds[hq_u[uu] * p.T_len + min(i_u[uu], p.T_len - 1)];
-  const float c2 = p.scale_log2;
-  const int jend = CAUSAL ? i : m_seq - 1;  // identical for both units
-  const size_t diag_row = ((size_t)(b * p.Hq + hq) * p.M + i) * p.M;
-
-  f32x16 o[C::DB];
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db) o[db] = f32x16{};
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  float lb_run = 0.f;
-  float mrun_u[2] = {-INFINITY, -INFINITY};  // per unit: largest s_max of its kept tiles (gap gate)
-  int nskip = 0;
-
-  u32x4 kreg[P2::LD];
-  u32x4 vreg[P2::LD];
-#pragma unroll
-  for (int it = 0; it < P2::LD; ++it) {
-    const int c = tid + P2::NT * it;
-    kreg[it] = kg[RAGGED ? tile_chunk<C::CPR>(0, c, n_seq) : c];
-  }
-#pragma unroll
-  for (int it = 0; it < P2::LD; ++it) {
-    const int c = tid + P2::NT * it;
-    *reinterpret_cast<u32x4*>(k_lds + (c / C::CPR) * C::KS + (c % C::CPR) * 16) = kreg[it];
-  }
-
-  // One key tile.  DIAGC is true only for the causal diagonal tile, the last
-  // one visited, so the masking of keys after the query is compiled into that
-  // single step and not evaluated (or predicated) on every other tile.
-  auto step = [&](const int j, auto DIAGC) {
-    constexpr bool DIAG_TILE = decltype(DIAGC)::value;
-    lds_barrier();  // (a): K_j (and Q) visible; every wave is done with V_{j-1}
-    const bool more = CAUSAL ? !DIAG_TILE : (j < jend);
-    if (more) {
-      const u32x4* src = kg + (size_t)(j + 1) * TILE_CHUNKS;
-#pragma unroll
-      for (int it = 0; it < P2::LD; ++it) {
-        const int c = tid + P2::NT * it;
-        kreg[it] = RAGGED ? kg[tile_chunk<C::CPR>((j + 1) * BLK, c, n_seq)] : src[c];
-      }
-    }
-    // ---- (a4) S^T = K_j Q^T ------------------------------------------------
-    f32x16 s[C::KB];
-    qk_tile_qlds<D, BLK>(s, k_lds, k_lane, q_lds[u], q_lane);
-    if constexpr (CAUSAL && DIAG_TILE) {
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key > qloc) s[kb][r] = -INFINITY;
-        }
-    }
-    if constexpr (RAGGED) {
-      const int rows_left = n_seq - i * BLK, keys_left = n_seq - j * BLK;
-      if (rows_left < BLK || keys_left < BLK) mask_tail(s, qloc, hh, rows_left, keys_left);
-    }
-    // ---- (a5) tile maxima of both units and their gates ---------------------
-    float rm0 = -INFINITY, rm1 = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        rm0 = fmaxf(rm0, s[kb][r]);
-        rm1 = fmaxf(rm1, s[kb][r + 1]);
-      }
-    float rm = fmaxf(rm0, rm1);
-    rm = fmaxf(rm, __shfl_xor(rm, 32));
-    float wm = rm;
-#pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) wm = fmaxf(wm, __shfl_xor(wm, off));
-    if (lane == 0) red[u][wu] = wm;
-    lds_barrier();  // (b): every wave is done with K_j; maxima complete
-    int skip_of[2];
-#pragma unroll
-    for (int uu = 0; uu < 2; ++uu) {
-      float tm = red[uu][0];
-#pragma unroll
-      for (int ww = 1; ww < P2::NWU; ++ww) tm = fmaxf(tm, red[uu][ww]);
-      const float tms = tm * p.scale;
-      skip_of[uu] = MAXONLY ? 1 : gate_skip(p.gate, j != i_u[uu], tms, tau_u[uu], mrun_u[uu]);
-      if (DIAG_OUT && uu == u && wu == 0 && lane == 0 && live) {
-        if (p.tile_state) p.tile_state[diag_row + j] = (j == i) ? 3 : (skip_of[uu] ? 2 : 1);
-        if (p.tile_max) p.tile_max[diag_row + j] = tms;
-      }
-    }
-    const int skip = __builtin_amdgcn_readfirstlane(u ? skip_of[1] : skip_of[0]);
-    const int need_v = __builtin_amdgcn_readfirstlane((skip_of[0] & skip_of[1]) ? 0 : 1);
-    // ---- (a8) V_j requested only if some unit keeps tile j -------------------
-    if (need_v) {
-      const u32x4* src = vg + (size_t)j * TILE_CHUNKS;
-#pragma unroll
-      for (int it = 0; it < P2::LD; ++it) {
-        const int c = tid + P2::NT * it;
-        vreg[it] = RAGGED ? vg[tile_chunk<C::CPR>(j * BLK, c, n_seq)] : src[c];
-      }
-    }
-    if (more) {
-#pragma unroll
-      for (int it = 0; it < P2::LD; ++it) {
-        const int c = tid + P2::NT * it;
-        *reinterpret_cast<u32x4*>(k_lds + (c / C::CPR) * C::KS + (c % C::CPR) * 16) = kreg[it];
-      }
-    }
-    bf16x8 pf[C::PC];
-    if (!skip) {
-      // ---- (a7) online softmax (lazy rescale, see the single-unit kernel) ----
-      const float m_tile = rm * c2;
-      const bool grow = m_tile > m_run + 4.f;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float m_new = grow ? m_tile : m_run;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-        lb_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
-        m_run = m_new;
-      }
-      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-      float rs0 = 0.f, rs1 = 0.f, rb0 = 0.f, rb1 = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-          for (int r = 0; r < 8; r += 2) {
-            f32x2 pr;
-            pr[0] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hf + r], c2, -m_run));
-            pr[1] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hf + r + 1], c2, -m_run));
-            const bf16x2 pb = __builtin_convertvector(pr, bf16x2);
-            rs0 += pr[0];
-            rs1 += pr[1];
-            if (r & 2) rb1 = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, rb1, false);
-            else rb0 = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, rb0, false);
-            pf[2 * kb + hf][r] = pb[0];
-            pf[2 * kb + hf][r + 1] = pb[1];
-          }
-      l_run += rs0 + rs1;
-      lb_run += rb0 + rb1;
-    } else {
-      ++nskip;  // (a6)
-    }
-    if (need_v) {
-#pragma unroll
-      for (int it = 0; it < P2::LD; ++it) {
-        const int c = tid + P2::NT * it;
-        const int row = c / C::CPR;
-        *reinterpret_cast<u32x4*>(v_lds + row * (2 * D) + ((c % C::CPR) ^ v_swz<D>(row)) * 16) = vreg[it];
-      }
-      lds_barrier();  // (c): V_j complete
-      if (!skip) {
-#pragma unroll
-        for (int kc = 0; kc < C::PC; ++kc)
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db) {
-            const int row = 16 * kc + v_row;
-            const int chunk = (4 * db + v_col) ^ v_swz<D>(row);
-            const char* base = v_lds + row * (2 * D) + chunk * 16 + v_half;
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * 2 * D));
-            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kc], o[db], 0, 0, 0);
-          }
-      }
-    }
-  };
-  if constexpr (CAUSAL) {
-    for (int j = 0; j < i; ++j) step(j, std::false_type{});
-    step(i, std::true_type{});
-  } else {
-    for (int j = 0; j <= jend; ++j) step(j, std::false_type{});
-  }
-
-  const int utid = wu * 64 + lane;  // thread index inside the unit
-  constexpr int UNT = P2::NWU * 64;
-  if (MAXONLY) {
-    if ((CAUSAL || RAGGED) && live)
-      for (int jj = jend + 1 + utid; jj < p.M; jj += UNT) p.tile_max[diag_row + jj] = __builtin_nanf("");
-    return;
-  }
-  // ---- (a9) epilogue -------------------------------------------------------
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.f / (lb_run + __shfl_xor(lb_run, 32));
-  if (!RAGGED || qrow < n_seq) {
-    store_out_row(p, q_head + qrow, o, inv, hh);
-    if (p.lse && hh == 0) p.lse[q_head + qrow] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
-  }
-  if (p.skip_counts && utid == 0 && live) p.skip_counts[(size_t)(b * p.Hq + hq) * p.M + i] = nskip;
-  if (DIAG_OUT && (CAUSAL || RAGGED) && live) {
-    for (int jj = jend + 1 + utid; jj < p.M; jj += UNT) {
-      if (p.tile_state) p.tile_state[diag_row + jj] = 0;
-      if (p.tile_max) p.tile_max[diag_row + jj] = __builtin_nanf("");
-    }
-  }
-}
-
-template <int D, int BLK, bool CAUSAL, bool DIAG_OUT, bool MAXONLY, bool RAGGED>
-static int launch_one(const FwdParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)((size_t)p.B * p.Hq * p.M));
-  const dim3 block(BLK * 2);
-  hipLaunchKernelGGL((bsfa_fwd_kernel<D, BLK, CAUSAL, DIAG_OUT, MAXONLY, RAGGED>), grid, block, 0, stream, p);
-  return hipGetLastError() == hipSuccess ? 0 : 5;
-}
-
-template <int D, int BLK, bool CAUSAL, bool DIAG_OUT, bool MAXONLY, bool HEADPAIR, bool RAGGED>
-static int launch_pair(FwdParams p, hipStream_t stream) {
-  const size_t units = (size_t)p.B * p.Hq * p.M;
-  const int per_group = HEADPAIR ? p.G / 2 : p.G;
-  p.remap = ((units / 2) % (8 * (size_t)per_group) == 0) ? 1 : 0;
-  const dim3 grid((unsigned)(units / 2));
-  const dim3 block(BLK * 4);
-  hipLaunchKernelGGL((bsfa_fwd_pair_kernel<D, BLK, CAUSAL, DIAG_OUT, MAXONLY, HEADPAIR, RAGGED>), grid, block, 0,
-                     stream, p);
-  return hipGetLastError() == hipSuccess ? 0 : 5;
-}
-
-// Two units per workgroup when they can share one K/V stream: query-head
-// pairs when the GQA group size is even, neighbouring query blocks of one head
-// when attention is bidirectional; otherwise one unit per workgroup.
-template <int D, int BLK, bool CAUSAL, bool DIAG_OUT, bool MAXONLY, bool RAGGED>
-static int launch_units_r(const FwdParams& p, hipStream_t s) {
-  if (p.G % 2 == 0) return launch_pair<D, BLK, CAUSAL, DIAG_OUT, MAXONLY, true, RAGGED>(p, s);
-  if (!CAUSAL && p.M % 2 == 0) return launch_pair<D, BLK, false, DIAG_OUT, MAXONLY, false, RAGGED>(p, s);
-  return launch_one<D, BLK, CAUSAL, DIAG_OUT, MAXONLY, RAGGED>(p, s);
-}
-
-// A sequence length that is not a multiple of the tile, or per-sequence
-// lengths, select the kernels compiled with the tail handling; aligned
-// lengths run without it.
-template <int D, int BLK, bool CAUSAL, bool DIAG_OUT, bool MAXONLY>
-static int launch_units(const FwdParams& p, hipStream_t s) {
-  if (p.N % BLK || p.seq_lens) return launch_units_r<D, BLK, CAUSAL, DIAG_OUT, MAXONLY, true>(p, s);
-  return launch_units_r<D, BLK, CAUSAL, DIAG_OUT, MAXONLY, false>(p, s);
-}
-
-// mode: 0 = forward, 1 = forward with per-tile diagnostics, 2 = tile maxima only
-template <int D, int BLK>
-static int launch_mode(const FwdParams& p, int causal, int mode, hipStream_t s) {
-  if (causal) {
-    if (mode == 2) return launch_units<D, BLK, true, true, true>(p, s);
-    return mode ? launch_units<D, BLK, true, true, false>(p, s) : launch_units<D, BLK, true, false, false>(p, s);
-  }
-  if (mode == 2) return launch_units<D, BLK, false, true, true>(p, s);
-  return mode ? launch_units<D, BLK, false, true, false>(p, s) : launch_units<D, BLK, false, false, false>(p, s);
-}
-
-int launch_fwd(const FwdParams& p, int head_dim, int block, int causal, int mode, hipStream_t stream) {
-  if (head_dim == 128 && block == 128) return launch_mode<128, 128>(p, causal, mode, stream);
-  if (head_dim == 128 && block == 64) return launch_mode<128, 64>(p, causal, mode, stream);
-  if (head_dim == 64 && block == 128) return launch_mode<64, 128>(p, causal, mode, stream);
-  if (head_dim == 64 && block == 64) return launch_mode<64, 64>(p, causal, mode, stream);
+int launch_fwd(const FwdParams& p, int head_dim, int bm, int bn, int causal, int mode, hipStream_t stream) {
+  if (bm == 128 && bn == 128) return launch_fwd_128x128(p, head_dim, causal, mode, stream);
+  if (bm == 128 && bn == 64) return launch_fwd_128x64(p, head_dim, causal, mode, stream);
+  if (bm == 64 && bn == 128) return launch_fwd_64x128(p, head_dim, causal, mode, stream);
+  if (bm == 64 && bn == 64) return launch_fwd_64x64(p, head_dim, causal, mode, stream);
   return 3;
 }
 

@@ -16,25 +16,36 @@ struct FwdParams {
   float* lse;         // fp32 [B, Hq, N] or null
   int32_t* skip_counts;     // int32 [B, Hq, M] or null
   const float* thresholds;  // fp32 [Hq, T_len]
-  uint8_t* tile_state;      // uint8 [B, Hq, M, M] or null (diagnostic launches only)
-  float* tile_max;          // fp32 [B, Hq, M, M] or null (diagnostic launches only)
+  uint8_t* tile_state;      // uint8 [B, Hq, M, Mkv] or null (diagnostic launches only)
+  float* tile_max;          // fp32 [B, Hq, M, Mkv] or null (diagnostic launches only)
   const int32_t* seq_lens;  // int32 [B] or null: per-sequence lengths (each clamped to [0, N])
-  int B, Hq, Hkv, G, N, M, T_len;
+  int B, Hq, Hkv, G, N, T_len;
+  int M;    // query blocks, ceil(N / B_M)
+  int Mkv;  // key blocks, ceil(N / B_N)
   float scale;       // 1 / sqrt(d)
   float scale_log2;  // scale * log2(e)
   int remap;         // 1: XCD-aware workgroup order applies (grid % (8 * G) == 0)
   int gate;          // 0: threshold gate (s_max < tau); 1: gap gate (s_max < running max - tau)
 };
 
-// Enqueue the forward kernel; mode 0 = forward, 1 = forward with per-tile
-// diagnostics, 2 = tile maxima only.  Returns a BSFA_* status.
-int launch_fwd(const FwdParams& p, int head_dim, int block, int causal, int mode, hipStream_t stream);
+// Enqueue the forward kernel for B_M x B_N tiles (bm, bn in {64, 128});
+// mode 0 = forward, 1 = forward with per-tile diagnostics, 2 = tile maxima
+// only.  Returns a BSFA_* status.
+int launch_fwd(const FwdParams& p, int head_dim, int bm, int bn, int causal, int mode, hipStream_t stream);
 
-// Enqueue the fixed-k calibration over tile maxima [S, H, M, M] -> thresholds [H, M].
-int launch_calibrate(const float* tile_max, int S, int H, int M, int causal, int k, float* thr,
-                     hipStream_t stream);
+// One translation unit per tile shape (bsfa_fwd_<bm>x<bn>.hip).
+int launch_fwd_128x128(const FwdParams& p, int head_dim, int causal, int mode, hipStream_t stream);
+int launch_fwd_128x64(const FwdParams& p, int head_dim, int causal, int mode, hipStream_t stream);
+int launch_fwd_64x128(const FwdParams& p, int head_dim, int causal, int mode, hipStream_t stream);
+int launch_fwd_64x64(const FwdParams& p, int head_dim, int causal, int mode, hipStream_t stream);
 
-// Largest number of query blocks the calibration kernel handles (one row of
+// Enqueue the fixed-k calibration over tile maxima [S, H, Mq, Mkv] ->
+// thresholds [H, Mq] for B_M x B_N tiles (bm = bn = 1 for square tiles of any
+// size: the diagonal of query block i is then key block i).
+int launch_calibrate(const float* tile_max, int S, int H, int Mq, int Mkv, int bm, int bn, int causal, int k,
+                     float* thr, hipStream_t stream);
+
+// Largest number of key blocks the calibration kernel handles (one row of
 // tile maxima must fit in LDS).
 constexpr int kCalibMaxBlocks = 16384;
 

@@ -9,8 +9,8 @@
  * threshold for its head and query block (Sec. 4, 4.1).  A tile below the
  * threshold is skipped: its V block is not loaded, the P.V product is not
  * performed and the running max / sum / output are not updated (Sec. 4.4).
- * Diagonal tiles always pass (Sec. 4.1).  Under causal masking, tiles above
- * the diagonal are not computed at all (App. B.2).
+ * Diagonal tiles always pass (Sec. 4.1).  Under causal masking, tiles with no
+ * visible (query, key) pair are not computed at all (App. B.2).
  *
  * Conventions shared by every entry point:
  *  - Tensor pointers are DEVICE pointers owned by the caller (for instance
@@ -41,9 +41,10 @@ typedef struct {
   int64_t batch;      /* B    >= 1 */
   int64_t n_heads_q;  /* H_q  >= 1 */
   int64_t n_heads_kv; /* H_kv >= 1, H_q % H_kv == 0 */
-  int64_t seq_len;    /* N    >= 1.  M = ceil(N / bm) query blocks and key blocks;
-                         when N is not a multiple of bm the last block of each
-                         is partial and positions >= N do not exist: they are
+  int64_t seq_len;    /* N    >= 1.  M = ceil(N / bm) query blocks and
+                         M_KV = ceil(N / bn) key blocks; when N is not a
+                         multiple of a tile side the last block is partial
+                         and positions >= N do not exist: they are
                          neither keys nor queries, take no part in any tile
                          maximum, and their output rows are not written.  (The
                          pages instead pad to a multiple of the tile by
@@ -55,8 +56,13 @@ typedef struct {
                          its last entry (App. B.3). */
 } bsfa_shape;
 
-/* Tile shape B_M x B_N (App. B.2).  This build supports square tiles with
- * bm == bn in {64, 128}; the tile is also the skip granularity. */
+/* Tile shape B_M x B_N (App. B.2): bm query rows by bn keys, each 64 or 128
+ * (square, or rectangular like the 128 x 64 tiles of the pages' A100 kernel,
+ * Sec. 5.1).  The tile is also the skip granularity: one gate per query
+ * block and key block.  The DIAGONAL tiles of query block i, which bypass the
+ * gate (Sec. 4.1), are the key blocks whose positions overlap the query
+ * block's: key block j with j*bn < (i+1)*bm and (j+1)*bn > i*bm (j = i for
+ * square tiles).  Thresholds are per query block. */
 typedef struct {
   int32_t bm;
   int32_t bn;
@@ -84,7 +90,7 @@ enum {
 
 /* Tile states written by bsfa_prefill_ex. */
 enum {
-  BSFA_TILE_PRUNED = 0,   /* causal: above the diagonal, never computed */
+  BSFA_TILE_PRUNED = 0,   /* causal: no visible pair (after the diagonal), never computed */
   BSFA_TILE_KEPT = 1,     /* off-diagonal, s_max >= threshold (or threshold NaN) */
   BSFA_TILE_SKIPPED = 2,  /* off-diagonal, s_max < threshold: no V load, no P.V */
   BSFA_TILE_DIAGONAL = 3  /* diagonal tile: bypasses the gate */
@@ -105,7 +111,7 @@ enum {
  *  skip_counts int32 [B, H_q, M] number of skipped tiles per query block;
  *                    NULL = not written
  *  thresholds  fp32  [H_q, T_len] in the scaled-score domain (the same units
- *                    as S).  Tile (i, j), j != i, is skipped iff
+ *                    as S).  A tile (i, j) off the diagonal is skipped iff
  *                    max_{visible (q,k) in tile} S[q,k] < thresholds[h, min(i, T_len-1)]
  *                    (strict, Sec. 4.4).  -inf keeps every tile (dense
  *                    attention); +inf keeps only the diagonal; NaN keeps all.
@@ -119,8 +125,8 @@ int bsfa_prefill(const void* q, const void* k, const void* v, float* out, float*
 
 /*
  * bsfa_prefill_ex - bsfa_prefill plus per-tile diagnostics (each nullable):
- *  tile_state uint8 [B, H_q, M, M] (M = ceil(N / bm)): BSFA_TILE_* of every tile
- *  tile_max   fp32  [B, H_q, M, M]: the gate's s_max (maximum scaled score over
+ *  tile_state uint8 [B, H_q, M, M_KV]: BSFA_TILE_* of every tile
+ *  tile_max   fp32  [B, H_q, M, M_KV]: the gate's s_max (maximum scaled score over
  *             the visible entries) of every computed tile, NaN where not computed.
  * Same contract as bsfa_prefill otherwise.  Slower: for testing and
  * calibration, not for production.
@@ -180,9 +186,10 @@ int bsfa_prefill_varlen(const void* q, const void* k, const void* v, float* out,
 /*
  * bsfa_tile_max - calibration pass: the tile maxima alone.
  *  q, k      as for bsfa_prefill
- *  tile_max  fp32 [B, H_q, M, M]: max over the visible entries of each computed
- *            tile of the scaled scores S = Q K^T / sqrt(d), NaN where a tile is
- *            not computed (causal, j > i).  Bit-identical to the tile_max output
+ *  tile_max  fp32 [B, H_q, M, M_KV]: max over the visible entries of each
+ *            computed tile of the scaled scores S = Q K^T / sqrt(d), NaN where a
+ *            tile is not computed (causal, no visible pair).  Bit-identical to
+ *            the tile_max output
  *            of bsfa_prefill_ex on the same inputs.
  * This is the measurement the threshold calibration of Sec. 4.2 sorts: "the
  * off-diagonal blocks ordered by their maximum scores".  QK^T only: no V is
@@ -192,8 +199,9 @@ int bsfa_tile_max(const void* q, const void* k, float* tile_max, bsfa_shape shap
                   void* stream);
 
 /*
- * bsfa_calibrate_fixed_k - fixed-k threshold table from tile maxima
- * (Sec. 4.2; App. B.3 "Threshold tensor").
+ * bsfa_calibrate_fixed_k - fixed-k threshold table from tile maxima of
+ * SQUARE tiles (Sec. 4.2; App. B.3 "Threshold tensor"); bsfa_calibrate
+ * covers every tile shape.
  *  tile_max    fp32 [S, H, M, M] device: tile maxima of S calibration samples
  *              (e.g. the batch of a bsfa_tile_max call), NaN-free on computed
  *              tiles
@@ -219,11 +227,37 @@ int bsfa_calibrate_fixed_k(const float* tile_max, int64_t n_samples, int64_t n_h
  *              bsfa_calibrate_fixed_k returns for k = ks[l].  Pass
  *              thresholds + l * H * M (with shape.thr_len = M) to bsfa_prefill
  *              to run at level l.
+ * Square tiles, as bsfa_calibrate_fixed_k.
  * Errors: as bsfa_calibrate_fixed_k, BSFA_ERR_NULL for ks == NULL,
  * BSFA_ERR_SHAPE for n_levels < 1 or a negative k.
  */
 int bsfa_calibrate_levels(const float* tile_max, int64_t n_samples, int64_t n_heads, int64_t n_blocks, int causal,
                           const int64_t* ks, int64_t n_levels, float* thresholds, void* stream);
+
+/*
+ * bsfa_calibrate - fixed-k threshold tensor for any tile shape and length
+ * (Sec. 4.2; App. B.3 "Threshold tensor").
+ *  tile_max    fp32 [B, H_q, M, M_KV] device: the output of bsfa_tile_max for
+ *              the same shape, causal flag and block; its B batch elements are
+ *              the calibration samples
+ *  shape, causal, block  as given to that bsfa_tile_max call (M = ceil(N/bm),
+ *              M_KV = ceil(N/bn))
+ *  ks          HOST array of n_levels values of k (each >= 0): off-diagonal
+ *              tiles kept per query block
+ *  thresholds  fp32 [n_levels, H_q, M] device, written.  Query block i has
+ *              n_i off-diagonal computed tiles: the key blocks that end
+ *              before it starts (causal), or every key block outside its
+ *              diagonal ones (bidirectional).  Entry (l, h, i) is -inf if
+ *              n_i <= ks[l], +inf if ks[l] == 0, otherwise the midpoint of the
+ *              k-th and (k+1)-th largest of those maxima, averaged over the B
+ *              samples.  For square tiles and N a multiple of bm this equals
+ *              bsfa_calibrate_levels.  Use slice l with shape.thr_len = M.
+ * Errors: as bsfa_validate for shape / causal / block; BSFA_ERR_NULL,
+ * BSFA_ERR_SHAPE (n_levels < 1, a negative k), BSFA_ERR_UNSUPPORTED
+ * (M_KV > 16384), BSFA_ERR_ALIGN.
+ */
+int bsfa_calibrate(const float* tile_max, bsfa_shape shape, int causal, bsfa_block block, const int64_t* ks,
+                   int64_t n_levels, float* thresholds, void* stream);
 
 /*
  * bsfa_validate - host-only check of a shape / mask / tile combination.

@@ -40,8 +40,14 @@ def away_from(t0: float, vals: np.ndarray, margin: float = 2e-3) -> float:
     return float(cand[np.argmin(np.abs(cand - t0))])
 
 
-def margin_thresholds(tile_max: np.ndarray, k, causal: bool, margin: float = 2e-3) -> np.ndarray:
-    """Fixed-k thresholds [H, M] (float32) from oracle tile maxima [B, H, M, M].
+def _diag(i: int, block, m_kv: int):
+    bm, bn = oracle.tile_shape(block)
+    return oracle.diagonal_blocks(i, bm, bn, m_kv)
+
+
+def margin_thresholds(tile_max: np.ndarray, k, causal: bool, margin: float = 2e-3, block=1) -> np.ndarray:
+    """Fixed-k thresholds [H, M] (float32) from oracle tile maxima [B, H, M, M_KV]
+    (``block``: the tile, for the diagonal sets; an int means square).
 
     Starts from the oracle's fixed-k calibration (averaged over the batch) and,
     where a tile maximum of any batch element lies within ``margin`` of it,
@@ -49,41 +55,44 @@ def margin_thresholds(tile_max: np.ndarray, k, causal: bool, margin: float = 2e-
     2*margin between consecutive off-diagonal maxima.  ``k=None`` gives -inf.
     Rows with no finite tile maxima keep the calibrated value.
     """
-    B, H, M, _ = tile_max.shape
+    B, H, M, M_kv = tile_max.shape
     if k is None:
         return np.full((H, M), -np.inf, dtype=np.float32)
-    thr = oracle.calibrate_fixed_k(tile_max, k, causal)
+    thr = oracle.calibrate_fixed_k(tile_max, k, causal, block)
     out = thr.astype(np.float32)
     for h in range(H):
         for i in range(M):
-            cols = [j for j in (range(i) if causal else range(M)) if j != i]
+            diag = _diag(i, block, M_kv)
+            cols = [j for j in range(M_kv) if j not in diag]
             out[h, i] = np.float32(away_from(float(out[h, i]), tile_max[:, h, i, cols].ravel(), margin))
     return out
 
 
 def gap_thresholds(tile_max: np.ndarray, causal: bool, base: float, margin: float = 2e-3,
-                   step: float = 0.037) -> np.ndarray:
+                   step: float = 0.037, block=1) -> np.ndarray:
     """Gaps [H, M] (float32) for the gap gate, starting at ``base``, moved per
     (head, query block) until no off-diagonal tile of any batch element lies
     within ``margin`` of its decision boundary M - gap (float64, the oracle's
     visiting order), so that the masks of the two sides must agree exactly."""
-    B, H, M, _ = tile_max.shape
+    B, H, M, M_kv = tile_max.shape
     out = np.empty((H, M), dtype=np.float32)
     for h in range(H):
         for i in range(M):
-            n = (i + 1) if causal else M
+            diag = _diag(i, block, M_kv)
             for t in range(200):
                 gap = np.float32(base + step * ((t + 1) // 2) * (1 if t % 2 else -1))
                 ok = True
                 for b in range(B):
-                    row = tile_max[b, h, i, :n]
+                    row = tile_max[b, h, i]
                     m = -np.inf
-                    for j in range(n):
+                    for j in range(M_kv):
+                        if not np.isfinite(row[j]):
+                            continue  # not computed
                         ref = m - float(gap)
-                        if j != i and np.isfinite(ref) and abs(row[j] - ref) <= margin:
+                        if j not in diag and np.isfinite(ref) and abs(row[j] - ref) <= margin:
                             ok = False
                             break
-                        if j == i or not row[j] < ref:
+                        if j in diag or not row[j] < ref:
                             m = max(m, row[j])
                     if not ok:
                         break
@@ -95,20 +104,10 @@ def gap_thresholds(tile_max: np.ndarray, causal: bool, base: float, margin: floa
     return out
 
 
-def exempt_tiles(oracle_tile_max: np.ndarray, thresholds: np.ndarray) -> np.ndarray:
-    """[B, H, M, M] bool: off-diagonal computed tiles whose s_max is within EXEMPT of tau."""
-    B, H, M, _ = oracle_tile_max.shape
-    t_len = thresholds.shape[1]
-    tau = thresholds[:, np.minimum(np.arange(M), t_len - 1)].astype(np.float64)  # [H, M]
-    near = np.abs(oracle_tile_max - tau[None, :, :, None]) <= EXEMPT
-    near &= np.isfinite(oracle_tile_max)
-    near[..., np.arange(M), np.arange(M)] = False
-    return near
-
-
-def compare_blocks(gpu: dict, ref_blocks, block: int, thresholds: np.ndarray, label: str = "",
+def compare_blocks(gpu: dict, ref_blocks, block, thresholds: np.ndarray, label: str = "",
                    exempt: bool = True):
-    """Compare GPU outputs (numpy, full arrays) with oracle ``run_blocks`` results.
+    """Compare GPU outputs (numpy, full arrays) with oracle ``run_blocks`` results
+    (``block``: an int for square tiles or (B_M, B_N)).
 
     ``exempt=False``: no tile is exempt from the mask comparison (inputs built
     with a margin around every decision boundary, e.g. ``gap_thresholds``).
@@ -121,9 +120,10 @@ def compare_blocks(gpu: dict, ref_blocks, block: int, thresholds: np.ndarray, la
     count = 0
     lse_worst = 0.0
     tmax_worst = 0.0
+    bm, _ = oracle.tile_shape(block)
     for r in ref_blocks:
         b, h, i = r["b"], r["h"], r["i"]
-        sl = slice(i * block, (i + 1) * block)
+        sl = slice(i * bm, (i + 1) * bm)
         computed = np.isfinite(r["tile_max"])
         st_ref = r["tile_state"]
         if "tile_state" in gpu:
@@ -131,7 +131,7 @@ def compare_blocks(gpu: dict, ref_blocks, block: int, thresholds: np.ndarray, la
             tau = float(thresholds[h, min(i, thresholds.shape[1] - 1)])
             near = np.zeros_like(computed)
             near[computed] = np.abs(r["tile_max"][computed] - tau) <= EXEMPT
-            near[i] = False
+            near[st_ref == oracle.STATE_DIAGONAL] = False
             if not exempt:
                 near[:] = False
             n_exempt += int(near.sum())

@@ -64,8 +64,36 @@ def test_validate(lib, shape, causal, blk, status):
     assert bb.bsfa_validate(shape, causal, bb.make_block(blk)) == status
 
 
-def test_rectangular_tile_unsupported(lib):
-    assert bb.bsfa_validate(S(), 1, bb.make_block(128, 64)) == 3
+def test_tile_shapes(lib):
+    # every pairing of 64 and 128 has kernels; other sides do not
+    for bm in (64, 128):
+        for bn in (64, 128):
+            assert bb.bsfa_validate(S(), 1, bb.make_block(bm, bn)) == 0
+            assert bb.bsfa_validate(S(N=1000), 0, bb.make_block(bm, bn)) == 0
+    for bm, bn in ((128, 32), (32, 128), (128, 224), (256, 64)):
+        assert bb.bsfa_validate(S(), 1, bb.make_block(bm, bn)) == 3
+    assert bb.bsfa_validate(S(), 1, bb.make_block(128, 0)) == 2
+    assert bb.bsfa_validate(S(), 1, bb.make_block(-64, 64)) == 2
+
+
+def test_calibrate_rejects_before_any_launch(lib):
+    import ctypes
+
+    good = 0x100000
+    ks = (ctypes.c_int64 * 2)(2, 5)
+    pks = ctypes.cast(ks, ctypes.c_void_p)
+    f = lib.bsfa_calibrate
+    blk = bb.make_block(128, 64)
+    assert f(good, S(), 1, bb.make_block(128, 32), pks, 2, good, None) == 3   # tile without kernels
+    assert f(good, S(Hq=3, Hkv=2), 1, blk, pks, 2, good, None) == 2           # shape
+    assert f(good, S(), 2, blk, pks, 2, good, None) == 2                      # causal flag
+    assert f(good, S(), 1, blk, None, 2, good, None) == 1                     # ks missing
+    assert f(None, S(), 1, blk, pks, 2, good, None) == 1                      # tile maxima missing
+    assert f(good, S(), 1, blk, pks, 0, good, None) == 2                      # no level
+    bad = (ctypes.c_int64 * 2)(3, -1)
+    assert f(good, S(), 1, blk, ctypes.cast(bad, ctypes.c_void_p), 2, good, None) == 2  # negative k
+    assert f(good, S(N=64 * 20000), 1, bb.make_block(128, 64), pks, 2, good, None) == 3  # M_KV beyond the kernel
+    assert f(good + 2, S(), 1, blk, pks, 2, good, None) == 4                  # misaligned tile maxima
 
 
 def test_status_strings(lib):
