@@ -20,7 +20,11 @@ Also reported, outside ``value``:
   * ``gate_study``: on the 32K inputs, the fixed-k points next to the gap gate
     (skip a tile below the running maximum minus a gap) at several gaps -
     realised skip fraction, time and error against the dense output
-    (``--no-gate-study`` skips it).
+    (``--no-gate-study`` skips it);
+  * ``tile_study``: on the same inputs, the sweep on 128 x 64 tiles (the
+    pages' A100 tile: finer skip granularity, half the work per gate) next
+    to 128 x 128 - skip fraction, time and error against the dense output
+    (``--no-tile-study`` skips it).
 
 Prints one JSON line.  ``--gpus N`` with N > 1 exits: this build runs on one GPU.
 """
@@ -47,8 +51,12 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
-    src = os.path.join(ROOT, "block_sparse_flashattention_tiled_amd", "csrc", "bsfa_fwd.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()
+    """sha256 over the forward kernel sources (template header and the 128 x 128 instantiation)."""
+    csrc = os.path.join(ROOT, "block_sparse_flashattention_tiled_amd", "csrc")
+    h = hashlib.sha256()
+    for f in ("bsfa_fwd_kernels.h", "bsfa_fwd_128x128.hip"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload: str):
@@ -112,7 +120,7 @@ def cpu_baseline(data, w, ks, budget_s):
 
 
 class Layer:
-    """Resident inputs, calibration and output buffers of one workload."""
+    """Resident inputs, calibration and output buffers of one workload on one tile shape."""
 
     def __init__(self, name, seed, torch, bb, wl, acc):
         self.torch, self.bb, self.acc = torch, bb, acc
@@ -122,20 +130,30 @@ class Layer:
         self.data = wl.generate(w, seed=seed)
         log(f"generated in {time.time() - t0:.1f} s; uploading")
         self.q, self.k, self.v = (bb.bits_to_device(self.data[n]) for n in ("q", "k", "v"))
-        self.M = w.n_blocks
-        self.shape = bb.make_shape(w.batch, w.heads_q, w.heads_kv, w.seq_len, w.head_dim, self.M)
-        self.block = bb.make_block(w.block)
-        self.tmax = bb.tile_max(self.q, self.k, w.causal, w.block)  # calibration pass (untimed)
         self.out = torch.empty((w.batch, w.heads_q, w.seq_len, w.head_dim), dtype=torch.float32, device="cuda")
         self.lse = torch.empty((w.batch, w.heads_q, w.seq_len), dtype=torch.float32, device="cuda")
         self.stream = torch.cuda.current_stream()
+        self.set_tile((w.block, w.block))
+
+    def set_tile(self, tile):
+        """Switch to B_M x B_N tiles: block counts, shape, and the calibration pass (untimed)."""
+        w, bb = self.w, self.bb
+        self.tile = tuple(tile)
+        self.M, self.Mkv = -(-w.seq_len // tile[0]), -(-w.seq_len // tile[1])
+        self.shape = bb.make_shape(w.batch, w.heads_q, w.heads_kv, w.seq_len, w.head_dim, self.M)
+        self.block = bb.make_block(*tile)
+        self.tmax = bb.tile_max(self.q, self.k, w.causal, self.tile)
 
     def fixed_k_points(self, targets):
+        w, (bm, bn) = self.w, self.tile
         points = []
         for tgt in targets:
-            kk = self.acc.k_for_target(self.M, tgt, self.w.causal)
-            thr = self.bb.calibrate_fixed_k(self.tmax, kk, self.w.causal)
-            points.append({"target": tgt, "k": kk, "thr": thr, "gate": "threshold"})
+            kk = self.acc.grid_k_for_target(w.seq_len, bm, bn, tgt, w.causal)
+            if kk is None:
+                thr = self.torch.full((w.heads_q, self.M), float("-inf"), dtype=self.torch.float32, device="cuda")
+            else:
+                thr = self.bb.calibrate(self.tmax, [kk], w.causal, self.tile, w.seq_len, w.head_dim)[0].contiguous()
+            points.append({"target": tgt, "k": kk, "thr": thr, "gate": "threshold", "tile": list(self.tile)})
         return points
 
     def launch(self, pt, counts, out=None):
@@ -173,17 +191,17 @@ class Layer:
         torch.cuda.synchronize()
         total_ms = t_start.elapsed_time(t_end)
         log(f"{w.name}: timed {steps} steps in {total_ms:.1f} ms")
-        M, blk, d = self.M, w.block, w.head_dim
-        dense_flops = acc.dense_equivalent_flops(w.batch, w.heads_q, M, blk, d, w.causal)
-        computed = acc.computed_tiles(M, w.causal) * w.batch * w.heads_q
+        (bm, bn), d, n = self.tile, w.head_dim, w.seq_len
+        dense_flops = acc.grid_executed_flops(w.batch, w.heads_q, n, bm, bn, d, 0, w.causal)
+        computed = acc.grid_computed_tiles(n, bm, bn, w.causal) * w.batch * w.heads_q
         for pi, pt in enumerate(points):
             durs = [ev[s][pi][0].elapsed_time(ev[s][pi][1]) for s in range(steps)]
             skipped = int(counts[pi].sum().item())
-            fl = acc.executed_flops(w.batch, w.heads_q, M, blk, d, skipped, w.causal)
+            fl = acc.grid_executed_flops(w.batch, w.heads_q, n, bm, bn, d, skipped, w.causal)
             pt.update(ms_mean=float(np.mean(durs)), ms_median=float(np.median(durs)), ms_min=float(np.min(durs)),
                       skipped_tiles=skipped, skip_fraction=skipped / computed, executed_flops=fl)
             if pt.get("k") is not None or pt["gate"] == "threshold":
-                pt["designed_skip_fraction"] = (acc.designed_skip_fraction(M, pt["k"], w.causal)
+                pt["designed_skip_fraction"] = (acc.grid_designed_skip_fraction(n, bm, bn, pt["k"], w.causal)
                                                 if pt.get("k") is not None else 0.0)
             pt["executed_tflops"] = fl / (pt["ms_mean"] * 1e-3) / 1e12
             pt["dense_equivalent_tflops"] = dense_flops / (pt["ms_mean"] * 1e-3) / 1e12
@@ -226,6 +244,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-128k", action="store_true", help="skip the 128K long-context leg")
     ap.add_argument("--no-gate-study", action="store_true", help="skip the gap-gate comparison")
+    ap.add_argument("--no-tile-study", action="store_true", help="skip the 128 x 64 tile comparison")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="also run one plain 1 GiB device copy, whose HBM counters calibrate the kernel's")
     args = ap.parse_args()
@@ -295,7 +314,7 @@ def main():
             "block": w.block,
             "causal": w.causal,
             "skip_targets": list(w.skip_targets),
-            "thresholds": "fixed-k, self-calibrated on the GPU (bsfa_tile_max + bsfa_calibrate_fixed_k)",
+            "thresholds": "fixed-k, self-calibrated on the GPU (bsfa_tile_max + bsfa_calibrate)",
         },
         "points": public(points),
         "roofline": {
@@ -308,12 +327,15 @@ def main():
         },
     }
 
-    # ---- gap gate next to the fixed-k table on the same inputs -----------------
-    if not args.no_gate_study:
+    # ---- the dense output: reference of both studies --------------------------
+    if not (args.no_gate_study and args.no_tile_study):
         ref_out = lay.out.clone()
         lay.launch(points[0], torch.empty((w.batch, w.heads_q, lay.M), dtype=torch.int32, device="cuda"), ref_out)
         torch.cuda.synchronize()
         ref_lse = lay.lse.clone()
+
+    # ---- gap gate next to the fixed-k table on the same inputs -----------------
+    if not args.no_gate_study:
         study = [dict(pt, gate="threshold") for pt in points[1:]]
         for gap in GAP_SWEEP:
             study.append({"target": None, "k": None, "gap": gap, "gate": "gap",
@@ -328,6 +350,25 @@ def main():
             "gap_gate": "skip tile j iff its maximum scaled score < (largest maximum of the kept tiles) - gap",
             "points": public(study),
         }
+
+    # ---- 128 x 64 tiles next to 128 x 128 on the same inputs --------------------
+    if not args.no_tile_study and w.block == 128:
+        sq = [dict(pt) for pt in points]
+        for pt in sq:
+            pt.update(lay.errors_vs(ref_out, ref_lse, pt))
+        lay.set_tile((128, 64))
+        rect = lay.fixed_k_points(targets)
+        lay.measure(rect, max(3, args.steps // 4), 1)
+        for pt in rect:
+            pt.update(lay.errors_vs(ref_out, ref_lse, pt))
+            pt["speedup_vs_dense"] = points[0]["ms_mean"] / pt["ms_mean"]
+        res["tile_study"] = {
+            "workload": w.name,
+            "reference": "the 128 x 128 kernel at threshold -inf; speedup_vs_dense relative to it",
+            "tiles": {"128x128": public(sq), "128x64": public(rect)},
+        }
+        lay.set_tile((w.block, w.block))
+    if not (args.no_gate_study and args.no_tile_study):
         del ref_out
 
     if not args.no_cpu_baseline:

@@ -15,7 +15,11 @@ statement of "Block Sparse Flash Attention" (paperpeel.com/paper/2512.07011):
 
 The fixed-k helpers count the tiles a fixed-k table is designed to skip: a
 query block with n off-diagonal computed tiles keeps min(k, n) of them plus
-its diagonal tile (Sec. 4, 4.1, 4.2).
+its diagonal tile (Sec. 4, 4.1, 4.2).  The ``grid_*`` helpers do the same for
+any tile B_M x B_N and length N (partial last blocks): the diagonal tiles of
+a query block are the key blocks overlapping its positions, and under causal
+masking a tile is computed when its first key is not after the block's last
+query.
 """
 
 from __future__ import annotations
@@ -39,6 +43,12 @@ __all__ = [
     "threshold_count",
     "threshold_table_bytes",
     "v_share_of_kv_traffic",
+    "grid_rows",
+    "grid_computed_tiles",
+    "grid_designed_skipped_tiles",
+    "grid_designed_skip_fraction",
+    "grid_k_for_target",
+    "grid_executed_flops",
 ]
 
 
@@ -154,3 +164,54 @@ def threshold_table_bytes(layers: int, heads: int, n_max: int, bm: int, levels: 
 def v_share_of_kv_traffic(bn: int, d: int) -> float:
     """Share of one tile's K+V load that a skip avoids: V_j over K_j + V_j (Sec. 4.3)."""
     return (bn * d) / (2 * bn * d)
+
+
+def grid_rows(n: int, bm: int, bn: int, causal: bool):
+    """Per query block of a length-``n`` sequence cut into ``bm`` x ``bn`` tiles:
+    (computed tiles, off-diagonal computed tiles)."""
+    m, m_kv = -(-n // bm), -(-n // bn)
+    rows = []
+    for i in range(m):
+        last_q = min((i + 1) * bm, n) - 1
+        computed = min(last_q // bn + 1, m_kv) if causal else m_kv
+        first_diag = (i * bm) // bn
+        last_diag = min(last_q // bn, m_kv - 1)
+        rows.append((computed, computed - (last_diag - first_diag + 1)))
+    return rows
+
+
+def grid_computed_tiles(n: int, bm: int, bn: int, causal: bool) -> int:
+    """Tiles computed for one head."""
+    return sum(c for c, _ in grid_rows(n, bm, bn, causal))
+
+
+def grid_designed_skipped_tiles(n: int, bm: int, bn: int, k: int, causal: bool) -> int:
+    """Tiles one head skips under a fixed-k table: sum_i max(0, n_i - k)."""
+    return sum(max(0, off - k) for _, off in grid_rows(n, bm, bn, causal))
+
+
+def grid_designed_skip_fraction(n: int, bm: int, bn: int, k: int, causal: bool) -> float:
+    return grid_designed_skipped_tiles(n, bm, bn, k, causal) / grid_computed_tiles(n, bm, bn, causal)
+
+
+def grid_k_for_target(n: int, bm: int, bn: int, target: float, causal: bool) -> Optional[int]:
+    """The k whose designed skip fraction is closest to ``target`` (None for 0: no gating;
+    ties go to the larger k)."""
+    if target <= 0.0:
+        return None
+    kmax = max(off for _, off in grid_rows(n, bm, bn, causal))
+    best_k, best_err = kmax, float("inf")
+    for k in range(kmax, -1, -1):
+        err = abs(grid_designed_skip_fraction(n, bm, bn, k, causal) - target)
+        if err < best_err - 1e-15:
+            best_k, best_err = k, err
+    return best_k
+
+
+def grid_executed_flops(batch: int, heads: int, n: int, bm: int, bn: int, d: int, skipped: int,
+                        causal: bool) -> int:
+    """MFMA FLOPs issued on full tiles: QK^T on every computed tile, P.V on kept ones
+    (partial tiles are counted whole, as the kernel computes them)."""
+    t = tile_matmul_flops(bm, bn, d)
+    comp = grid_computed_tiles(n, bm, bn, causal) * batch * heads
+    return comp * t + (comp - skipped) * t

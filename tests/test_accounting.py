@@ -99,3 +99,49 @@ def test_executed_flops_counts_kept_pv_only():
     t = acc.tile_matmul_flops(blk, blk, d)
     comp = acc.computed_tiles(m, True) * b * h
     assert acc.executed_flops(b, h, m, blk, d, 10, True) == 2 * comp * t - 10 * t
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_grid_counts_reduce_to_the_square_ones(causal):
+    for m in (1, 2, 7, 64):
+        n = 128 * m
+        assert acc.grid_computed_tiles(n, 128, 128, causal) == acc.computed_tiles(m, causal)
+        for k in (0, 1, 5, m + 3):
+            assert acc.grid_designed_skipped_tiles(n, 128, 128, k, causal) == \
+                acc.designed_skipped_tiles(m, k, causal)
+        for tgt in (0.0, 0.6, 0.9):
+            assert acc.grid_k_for_target(n, 128, 128, tgt, causal) == acc.k_for_target(m, tgt, causal)
+        assert acc.grid_executed_flops(2, 3, n, 128, 128, 64, 11, causal) == \
+            acc.executed_flops(2, 3, m, 128, 64, 11, causal)
+
+
+def _brute_grid(n, bm, bn, causal):
+    """(computed, off-diagonal) per query block by enumerating positions."""
+    m, m_kv = -(-n // bm), -(-n // bn)
+    rows = []
+    for i in range(m):
+        qs = range(i * bm, min((i + 1) * bm, n))
+        comp = off = 0
+        for j in range(m_kv):
+            ks = range(j * bn, min((j + 1) * bn, n))
+            if causal and not any(kk <= qq for qq in qs for kk in ks):
+                continue
+            comp += 1
+            off += 0 if set(qs) & set(ks) else 1
+        rows.append((comp, off))
+    return rows
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("n,bm,bn", [(1024, 128, 64), (1000, 128, 64), (960, 64, 128), (77, 128, 64),
+                                     (300, 48, 32), (256, 32, 48)])
+def test_grid_rows_by_enumeration(n, bm, bn, causal):
+    assert acc.grid_rows(n, bm, bn, causal) == _brute_grid(n, bm, bn, causal)
+
+
+def test_grid_128x64_causal_closed_form():
+    # query block i of 128 rows sees key blocks 0..2i+1 of 64 keys, two of them diagonal
+    m = 16
+    rows = acc.grid_rows(128 * m, 128, 64, True)
+    assert rows == [(2 * i + 2, 2 * i) for i in range(m)]
+    assert acc.grid_computed_tiles(128 * m, 128, 64, True) == m * (m + 1)
