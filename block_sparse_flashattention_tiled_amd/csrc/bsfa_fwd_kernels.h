@@ -359,6 +359,16 @@ __global__ void __launch_bounds__(BM * 2) bsfa_fwd_kernel(const FwdParams p) {
       if (p.tile_state) p.tile_state[diag_row + j] = diag ? 3 : (skip ? 2 : 1);
       if (p.tile_max) p.tile_max[diag_row + j] = tms;
     }
+    // K_{j+1} -> LDS (every wave has finished reading K_j), before V_j is
+    // requested: loads complete in issue order, so waiting for K_{j+1} after
+    // the V_j requests would also wait for V_j
+    if (more) {
+#pragma unroll
+      for (int it = 0; it < C::LD; ++it) {
+        const int c = tid + C::NT * it;
+        *reinterpret_cast<u32x4*>(k_lds + (c / C::CPR) * C::KS + (c % C::CPR) * 16) = kreg[it];
+      }
+    }
     // ---- (a8) V_j requested only for a kept tile ---------------------------
     if (!skip) {
       const u32x4* src = vg + (size_t)j * TILE_CHUNKS;
@@ -366,14 +376,6 @@ __global__ void __launch_bounds__(BM * 2) bsfa_fwd_kernel(const FwdParams p) {
       for (int it = 0; it < C::LD; ++it) {
         const int c = tid + C::NT * it;
         vreg[it] = RAGGED ? vg[tile_chunk<C::CPR>(j * BN, c, n_seq)] : src[c];
-      }
-    }
-    // K_{j+1} -> LDS (every wave has finished reading K_j)
-    if (more) {
-#pragma unroll
-      for (int it = 0; it < C::LD; ++it) {
-        const int c = tid + C::NT * it;
-        *reinterpret_cast<u32x4*>(k_lds + (c / C::CPR) * C::KS + (c % C::CPR) * 16) = kreg[it];
       }
     }
     if (skip) {  // (a6): no V load, no exp, no statistics update
@@ -689,6 +691,16 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
     }
     const int skip = __builtin_amdgcn_readfirstlane(u ? skip_of[1] : skip_of[0]);
     const int need_v = __builtin_amdgcn_readfirstlane((skip_of[0] & skip_of[1]) ? 0 : 1);
+    // K_{j+1} -> LDS before V_j is requested: vector loads complete in issue
+    // order, so waiting for K_{j+1} after the V_j requests would also wait for
+    // V_j, whose latency is meant to hide behind the softmax
+    if (more) {
+#pragma unroll
+      for (int it = 0; it < P2::LD; ++it) {
+        const int c = tid + P2::NT * it;
+        *reinterpret_cast<u32x4*>(k_lds + (c / C::CPR) * C::KS + (c % C::CPR) * 16) = kreg[it];
+      }
+    }
     // ---- (a8) V_j requested only if some unit keeps tile j -------------------
     if (need_v) {
       const u32x4* src = vg + (size_t)j * TILE_CHUNKS;
@@ -696,13 +708,6 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
       for (int it = 0; it < P2::LD; ++it) {
         const int c = tid + P2::NT * it;
         vreg[it] = RAGGED ? vg[tile_chunk<C::CPR>(j * BN, c, n_seq)] : src[c];
-      }
-    }
-    if (more) {
-#pragma unroll
-      for (int it = 0; it < P2::LD; ++it) {
-        const int c = tid + P2::NT * it;
-        *reinterpret_cast<u32x4*>(k_lds + (c / C::CPR) * C::KS + (c % C::CPR) * 16) = kreg[it];
       }
     }
     bf16x8 pf[C::PC];
