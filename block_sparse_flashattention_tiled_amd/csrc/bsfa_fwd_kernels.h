@@ -513,13 +513,22 @@ __device__ __forceinline__ void qk_tile_qlds(f32x16 (&s)[NKB], const char* ks, i
 template <int D, int BM, int BN, bool CAUSAL, bool DIAG_OUT, bool MAXONLY, bool HEADPAIR, bool RAGGED>
 __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 2)))
     bsfa_fwd_pair_kernel(const FwdParams p) {
-  using C = Cfg<D, BM, BN>;
-  using P2 = PairCfg<D, BM, BN>;
+  // Key tiles per step: 128 x 64 tiles are processed two per 128-key step, so
+  // the barriers and the MFMA sequence are those of 128 x 128 tiles, while each
+  // 64-key tile keeps its own gate, V request, softmax and P.V.
+  constexpr int SUB = (BM == 128 && BN == 64) ? 2 : 1;
+  constexpr int KN = SUB * BN;  // keys per step
+  using C = Cfg<D, BM, KN>;
+  using P2 = PairCfg<D, BM, KN>;
+  constexpr int KBS = C::KB / SUB;      // 32-key sub-blocks per key tile
+  constexpr int PCS = C::PC / SUB;      // 16-key P.V chunks per key tile
+  constexpr int RPI = P2::NT / C::CPR;  // K / V rows per load iteration
+  static_assert(BN % RPI == 0 || SUB == 1, "a V load iteration stays inside one key tile");
   static_assert(HEADPAIR || !CAUSAL, "block pairs are for bidirectional attention");
   __shared__ __attribute__((aligned(16))) char q_lds[2][P2::Q_BYTES];
   __shared__ __attribute__((aligned(16))) char k_lds[C::K_BYTES];
   __shared__ __attribute__((aligned(16))) char v_lds[C::V_BYTES];
-  __shared__ float red[2][P2::NWU];
+  __shared__ float red[2][P2::NWU][SUB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -609,7 +618,8 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
     jd0_u[uu] = diag_first<BM, BN>(i_u[uu]);
     jd1_u[uu] = diag_last<BM, BN>(i_u[uu], mkv_seq);
   }
-  const int jend = CAUSAL ? jd1_u[0] : mkv_seq - 1;
+  const int jend = CAUSAL ? jd1_u[0] : mkv_seq - 1;  // last computed key tile
+  const int send = jend / SUB;                        // last step
   const size_t diag_row = ((size_t)(b * p.Hq + hq) * p.M + i) * p.Mkv;
 
   f32x16 o[C::DB];
@@ -634,63 +644,84 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
     *reinterpret_cast<u32x4*>(k_lds + (c / C::CPR) * C::KS + (c % C::CPR) * 16) = kreg[it];
   }
 
-  // One key tile.  DIAGC is true only for the causal diagonal tiles, the last
-  // ones visited, so the masking of keys after the query is compiled into
-  // those steps and not evaluated (or predicated) on every other tile.
-  auto step = [&](const int j, auto DIAGC) {
+  // One step: key tiles SUB*js .. SUB*js + SUB - 1.  DIAGC is true only for the
+  // causal diagonal step(s), the last visited, so the masking of keys after the
+  // query is compiled into those steps and not evaluated (or predicated) on
+  // every other step.
+  auto step = [&](const int js, auto DIAGC) {
     constexpr bool DIAG_TILE = decltype(DIAGC)::value;
-    lds_barrier();  // (a): K_j (and Q) visible; every wave is done with V_{j-1}
-    // causal: a tile before the diagonal always has a successor; with one
-    // diagonal tile the diagonal step is the last
-    const bool more = CAUSAL ? (!DIAG_TILE || (C::ND > 1 && j < jend)) : (j < jend);
+    lds_barrier();  // (a): K_js (and Q) visible; every wave is done with V_{js-1}
+    // causal: a step before the diagonal always has a successor; with one
+    // diagonal step it is the last
+    const bool more = CAUSAL ? (!DIAG_TILE || (C::ND > 1 && js < send)) : (js < send);
     if (more) {
-      const u32x4* src = kg + (size_t)(j + 1) * TILE_CHUNKS;
+      const u32x4* src = kg + (size_t)(js + 1) * TILE_CHUNKS;
 #pragma unroll
       for (int it = 0; it < P2::LD; ++it) {
         const int c = tid + P2::NT * it;
-        kreg[it] = RAGGED ? kg[tile_chunk<C::CPR>((j + 1) * BN, c, n_seq)] : src[c];
+        kreg[it] = RAGGED ? kg[tile_chunk<C::CPR>((js + 1) * KN, c, n_seq)] : src[c];
       }
     }
-    // ---- (a4) S^T = K_j Q^T ------------------------------------------------
+    // ---- (a4) S^T = K Q^T over the step's keys -------------------------------
     f32x16 s[C::KB];
-    qk_tile_qlds<D, BM, BN>(s, k_lds, k_lane, q_lds[u], q_lane);
-    if constexpr (CAUSAL && DIAG_TILE) mask_causal(s, qloc, hh, i * BM - j * BN);
+    qk_tile_qlds<D, BM, KN>(s, k_lds, k_lane, q_lds[u], q_lane);
+    if constexpr (CAUSAL && DIAG_TILE) mask_causal(s, qloc, hh, i * BM - js * KN);
     if constexpr (RAGGED) {
-      const int rows_left = n_seq - i * BM, keys_left = n_seq - j * BN;
-      if (rows_left < BM || keys_left < BN) mask_tail(s, qloc, hh, rows_left, keys_left);
+      const int rows_left = n_seq - i * BM, keys_left = n_seq - js * KN;
+      if (rows_left < BM || keys_left < KN) mask_tail(s, qloc, hh, rows_left, keys_left);
     }
     // ---- (a5) tile maxima of both units and their gates ---------------------
-    float rm0 = -INFINITY, rm1 = -INFINITY;
+    float rm_t[SUB];  // this lane's row maximum over each key tile of the step
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
+    for (int t = 0; t < SUB; ++t) {
+      float rm0 = -INFINITY, rm1 = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        rm0 = fmaxf(rm0, s[kb][r]);
-        rm1 = fmaxf(rm1, s[kb][r + 1]);
-      }
-    float rm = fmaxf(rm0, rm1);
-    rm = fmaxf(rm, __shfl_xor(rm, 32));
-    float wm = rm;
+      for (int kb = t * KBS; kb < (t + 1) * KBS; ++kb)
 #pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) wm = fmaxf(wm, __shfl_xor(wm, off));
-    if (lane == 0) red[u][wu] = wm;
-    lds_barrier();  // (b): every wave is done with K_j; maxima complete
-    int skip_of[2];
+        for (int r = 0; r < 16; r += 2) {
+          rm0 = fmaxf(rm0, s[kb][r]);
+          rm1 = fmaxf(rm1, s[kb][r + 1]);
+        }
+      float rm = fmaxf(rm0, rm1);
+      rm = fmaxf(rm, __shfl_xor(rm, 32));
+      rm_t[t] = rm;
+      float wm = rm;
 #pragma unroll
-    for (int uu = 0; uu < 2; ++uu) {
-      float tm = red[uu][0];
-#pragma unroll
-      for (int ww = 1; ww < P2::NWU; ++ww) tm = fmaxf(tm, red[uu][ww]);
-      const float tms = tm * p.scale;
-      const bool on_diag = j >= jd0_u[uu] && j <= jd1_u[uu];
-      skip_of[uu] = MAXONLY ? 1 : gate_skip(p.gate, !on_diag, tms, tau_u[uu], mrun_u[uu]);
-      if (DIAG_OUT && uu == u && wu == 0 && lane == 0 && live) {
-        if (p.tile_state) p.tile_state[diag_row + j] = on_diag ? 3 : (skip_of[uu] ? 2 : 1);
-        if (p.tile_max) p.tile_max[diag_row + j] = tms;
-      }
+      for (int off = 16; off >= 1; off >>= 1) wm = fmaxf(wm, __shfl_xor(wm, off));
+      if (lane == 0) red[u][wu][t] = wm;
     }
-    const int skip = __builtin_amdgcn_readfirstlane(u ? skip_of[1] : skip_of[0]);
-    const int need_v = __builtin_amdgcn_readfirstlane((skip_of[0] & skip_of[1]) ? 0 : 1);
+    lds_barrier();  // (b): every wave is done with K_js; maxima complete
+    // gates in increasing key-tile order (the gap gate's running maximum)
+    int skip_of[2][SUB];
+#pragma unroll
+    for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+      for (int t = 0; t < SUB; ++t) {
+        const int j = js * SUB + t;
+        const bool exists = SUB == 1 || j < mkv_seq;  // the last step may hold a tile past the end
+        float tm = red[uu][0][t];
+#pragma unroll
+        for (int ww = 1; ww < P2::NWU; ++ww) tm = fmaxf(tm, red[uu][ww][t]);
+        const float tms = tm * p.scale;
+        const bool on_diag = j >= jd0_u[uu] && j <= jd1_u[uu];
+        skip_of[uu][t] = (MAXONLY || !exists) ? 1 : gate_skip(p.gate, !on_diag, tms, tau_u[uu], mrun_u[uu]);
+        if (DIAG_OUT && exists && uu == u && wu == 0 && lane == 0 && live) {
+          if (p.tile_state) p.tile_state[diag_row + j] = on_diag ? 3 : (skip_of[uu][t] ? 2 : 1);
+          if (p.tile_max) p.tile_max[diag_row + j] = tms;
+        }
+      }
+    // kmask: key tiles this unit keeps; vmask: key tiles some unit keeps
+    int km = 0, vm = 0, ns = 0;
+#pragma unroll
+    for (int t = 0; t < SUB; ++t) {
+      const int mine = u ? skip_of[1][t] : skip_of[0][t];
+      km |= (mine ? 0 : 1) << t;
+      vm |= ((skip_of[0][t] & skip_of[1][t]) ? 0 : 1) << t;
+      ns += (mine && (SUB == 1 || js * SUB + t < mkv_seq)) ? 1 : 0;
+    }
+    const int kmask = __builtin_amdgcn_readfirstlane(km);
+    const int vmask = __builtin_amdgcn_readfirstlane(vm);
+    nskip += ns;  // (a6)
     // K_{j+1} -> LDS before V_j is requested: vector loads complete in issue
     // order, so waiting for K_{j+1} after the V_j requests would also wait for
     // V_j, whose latency is meant to hide behind the softmax
@@ -701,18 +732,24 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
         *reinterpret_cast<u32x4*>(k_lds + (c / C::CPR) * C::KS + (c % C::CPR) * 16) = kreg[it];
       }
     }
-    // ---- (a8) V_j requested only if some unit keeps tile j -------------------
-    if (need_v) {
-      const u32x4* src = vg + (size_t)j * TILE_CHUNKS;
+    // ---- (a8) V of a key tile requested only if some unit keeps the tile -----
+    if (vmask) {
+      const u32x4* src = vg + (size_t)js * TILE_CHUNKS;
 #pragma unroll
       for (int it = 0; it < P2::LD; ++it) {
         const int c = tid + P2::NT * it;
-        vreg[it] = RAGGED ? vg[tile_chunk<C::CPR>(j * BN, c, n_seq)] : src[c];
+        if (SUB == 1 || ((vmask >> ((it * RPI) / BN)) & 1))
+          vreg[it] = RAGGED ? vg[tile_chunk<C::CPR>(js * KN, c, n_seq)] : src[c];
       }
     }
     bf16x8 pf[C::PC];
-    if (!skip) {
-      // ---- (a7) online softmax (lazy rescale, see the single-unit kernel) ----
+    if (kmask) {
+      // ---- (a7) online softmax over the kept key tiles (lazy rescale, see the
+      // single-unit kernel) --------------------------------------------------
+      float rm = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < SUB; ++t)
+        if (SUB == 1 || ((kmask >> t) & 1)) rm = fmaxf(rm, rm_t[t]);
       const float m_tile = rm * c2;
       const bool grow = m_tile > m_run + 4.f;
       if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -727,7 +764,8 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
       const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
       float rs0 = 0.f, rs1 = 0.f, rb0 = 0.f, rb1 = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
+      for (int kb = 0; kb < C::KB; ++kb) {
+        if (SUB > 1 && !((kmask >> (kb / KBS)) & 1)) continue;
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
@@ -743,22 +781,23 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
             pf[2 * kb + hf][r] = pb[0];
             pf[2 * kb + hf][r + 1] = pb[1];
           }
+      }
       l_run += rs0 + rs1;
       lb_run += rb0 + rb1;
-    } else {
-      ++nskip;  // (a6)
     }
-    if (need_v) {
+    if (vmask) {
 #pragma unroll
       for (int it = 0; it < P2::LD; ++it) {
         const int c = tid + P2::NT * it;
         const int row = c / C::CPR;
-        *reinterpret_cast<u32x4*>(v_lds + row * (2 * D) + ((c % C::CPR) ^ v_swz<D>(row)) * 16) = vreg[it];
+        if (SUB == 1 || ((vmask >> ((it * RPI) / BN)) & 1))
+          *reinterpret_cast<u32x4*>(v_lds + row * (2 * D) + ((c % C::CPR) ^ v_swz<D>(row)) * 16) = vreg[it];
       }
-      lds_barrier();  // (c): V_j complete
-      if (!skip) {
+      lds_barrier();  // (c): V of the step's kept tiles complete
+      if (kmask) {
 #pragma unroll
-        for (int kc = 0; kc < C::PC; ++kc)
+        for (int kc = 0; kc < C::PC; ++kc) {
+          if (SUB > 1 && !((kmask >> (kc / PCS)) & 1)) continue;
 #pragma unroll
           for (int db = 0; db < C::DB; ++db) {
             const int row = 16 * kc + v_row;
@@ -769,18 +808,22 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
             const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kc], o[db], 0, 0, 0);
           }
+        }
       }
     }
   };
   if constexpr (CAUSAL) {
-    for (int j = 0; j < jd0_u[0]; ++j) step(j, std::false_type{});
+    // the steps holding diagonal tiles come last; with SUB > 1 the diagonal
+    // tiles of a query block fill exactly one step
+    const int sd0 = jd0_u[0] / SUB;
+    for (int js = 0; js < sd0; ++js) step(js, std::false_type{});
     if constexpr (C::ND == 1) {
-      step(jend, std::true_type{});  // the only diagonal tile: jd0 == jend
+      step(send, std::true_type{});  // the only diagonal step: sd0 == send
     } else {
-      for (int j = jd0_u[0]; j <= jend; ++j) step(j, std::true_type{});
+      for (int js = sd0; js <= send; ++js) step(js, std::true_type{});
     }
   } else {
-    for (int j = 0; j <= jend; ++j) step(j, std::false_type{});
+    for (int js = 0; js <= send; ++js) step(js, std::false_type{});
   }
 
   const int utid = wu * 64 + lane;  // thread index inside the unit
