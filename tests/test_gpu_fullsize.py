@@ -32,43 +32,56 @@ def _sample_blocks(w, n, seed):
     return out
 
 
-@pytest.mark.parametrize("name", list(SAMPLES))
-def test_fullsize_sampled_parity(name):
+def _fullsize(name, tile, targets, n_samples):
     assert torch.cuda.is_available()
     w = wl.get_config(name)
-    print(f"[fullsize {name}] generating", flush=True)
+    bm, bn = tile
+    print(f"[fullsize {name} {bm}x{bn}] generating", flush=True)
     data = wl.generate(w, seed=0)
-    M = w.n_blocks
-    blocks = _sample_blocks(w, SAMPLES[name], seed=7)
+    M, M_kv = -(-w.seq_len // bm), -(-w.seq_len // bn)
+    blocks = _sample_blocks(w.replace(block=bm), n_samples, seed=7)
     rows = {}
     for b, h, i in blocks:
-        rows[(b, h, i)] = oracle.tile_maxima(data["q"][b:b + 1], data["k"][b:b + 1], w.causal, w.block,
+        rows[(b, h, i)] = oracle.tile_maxima(data["q"][b:b + 1], data["k"][b:b + 1], w.causal, tile,
                                              heads=[h], rows=[i])[0, h, i]
     q, k, v = (bb.bits_to_device(data[n]) for n in ("q", "k", "v"))
-    targets = [t for t in w.skip_targets if t > 0] or [0.0]
     for tgt in targets:
-        kk = acc.k_for_target(M, tgt, w.causal)
+        kk = acc.grid_k_for_target(w.seq_len, bm, bn, tgt, w.causal)
         thr = np.full((w.heads_q, M), np.nan, dtype=np.float64)
         for (b, h, i), tm_row in rows.items():
-            t0 = -np.inf if kk is None else oracle.calibrate_row(tm_row, i, kk, w.causal)
-            cols = [j for j in (range(i) if w.causal else range(M)) if j != i]
+            t0 = -np.inf if kk is None else oracle.calibrate_row(tm_row, i, kk, w.causal, tile)
+            diag = oracle.diagonal_blocks(i, bm, bn, M_kv)
+            cols = [j for j in range(M_kv) if j not in diag]
             thr[h, i] = away_from(float(np.float32(t0)), tm_row[cols])
         # rows that are not checked: the median of the checked ones (a valid input all the same)
         fill = np.nanmedian(np.where(np.isfinite(thr), thr, np.nan)) if np.isfinite(thr).any() else -np.inf
         thr = np.where(np.isnan(thr), fill, thr).astype(np.float32)
-        res = bb.prefill(q, k, v, torch.from_numpy(thr).cuda(), w.causal, w.block)
+        res = bb.prefill(q, k, v, torch.from_numpy(thr).cuda(), w.causal, tile)
         torch.cuda.synchronize()
         gpu = {n: t.cpu().numpy() for n, t in res.items()}
-        ref = oracle.run_blocks(data["q"], data["k"], data["v"], thr, w.causal, w.block, blocks)
-        stats = compare_blocks(gpu, ref, w.block, thr, f"{name}@{tgt}")
-        print(f"[fullsize {name} target {tgt} k={kk}] {stats} skip fraction "
-              f"{gpu['skip_counts'].sum() / (acc.computed_tiles(M, w.causal) * w.batch * w.heads_q):.4f}",
-              flush=True)
+        ref = oracle.run_blocks(data["q"], data["k"], data["v"], thr, w.causal, tile, blocks)
+        stats = compare_blocks(gpu, ref, tile, thr, f"{name}@{tgt}")
+        computed = acc.grid_computed_tiles(w.seq_len, bm, bn, w.causal) * w.batch * w.heads_q
+        print(f"[fullsize {name} {bm}x{bn} target {tgt} k={kk}] {stats} skip fraction "
+              f"{gpu['skip_counts'].sum() / computed:.4f}", flush=True)
         assert np.isfinite(gpu["out"]).all() and np.isfinite(gpu["lse"]).all()
-        n_off = np.array([i if w.causal else M - 1 for i in range(M)])
+        n_off = np.array([off for _, off in acc.grid_rows(w.seq_len, bm, bn, w.causal)])
         assert (gpu["skip_counts"] >= 0).all() and (gpu["skip_counts"] <= n_off[None, None, :]).all()
         if name == "llama32k":
-            again = bb.prefill(q, k, v, torch.from_numpy(thr).cuda(), w.causal, w.block)
+            again = bb.prefill(q, k, v, torch.from_numpy(thr).cuda(), w.causal, tile)
             torch.cuda.synchronize()
             for n in ("out", "lse", "skip_counts"):
                 assert np.array_equal(again[n].cpu().numpy(), gpu[n]), f"{n} not reproducible"
+
+
+@pytest.mark.parametrize("name", list(SAMPLES))
+def test_fullsize_sampled_parity(name):
+    w = wl.get_config(name)
+    # the layers the benchmark times are also checked at their dense point (threshold -inf)
+    targets = sorted(set(w.skip_targets) | ({0.0} if name in ("llama32k", "gqa128k") else set()))
+    _fullsize(name, (w.block, w.block), targets, SAMPLES[name])
+
+
+def test_fullsize_sampled_parity_128x64():
+    # the benchmark's tile study: the 32K layer on the pages' 128 x 64 tiles
+    _fullsize("llama32k", (128, 64), [0.0, 0.6, 0.9], 16)
