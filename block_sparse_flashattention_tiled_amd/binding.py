@@ -326,7 +326,8 @@ def tile_max(q: torch.Tensor, k: torch.Tensor, causal: bool, block, stream=None)
 
 
 def calibrate_fixed_k(tile_maxima: torch.Tensor, k: Optional[int], causal: bool, stream=None) -> torch.Tensor:
-    """Fixed-k threshold table [H, M] from tile maxima [S, H, M, M]; k=None gives -inf (dense)."""
+    """Fixed-k threshold table [H, M] from square-tile maxima [S, H, M, M]; k=None gives -inf (dense).
+    Any tile shape: ``calibrate``."""
     S, H, M, _ = tile_maxima.shape
     if k is None:
         return torch.full((H, M), float("-inf"), dtype=torch.float32, device=tile_maxima.device)

@@ -14,19 +14,26 @@
 // positions overlap the query block's: j = i for square tiles, and for
 // B_M != B_N every j with j B_N < (i+1) B_M and (j+1) B_N > i B_M.
 //
+// Two kernels share this arithmetic.  The paired kernel (further below) runs
+// two query units per workgroup on one K/V stream and is the production path
+// whenever units can be paired (an even GQA group, or bidirectional attention
+// with an even number of query blocks); the one-unit kernel serves the rest.
+//
 // Mapping onto CDNA4:
-//  * one workgroup per (batch, query head, query block); B_M/32 waves, wave w
-//    owns query rows [32w, 32w+32) of the block.  The kernel is sized to run
-//    two workgroups per CU (LDS < 80 KB, <= 256 registers per lane) so that
-//    one workgroup's MFMA phases overlap the other's softmax and waits;
+//  * one-unit kernel: one workgroup per (batch, query head, query block);
+//    B_M/32 waves, wave w owns query rows [32w, 32w+32) of the block.  It is
+//    sized to run two workgroups per CU (LDS < 80 KB, <= 256 registers per
+//    lane) so that one workgroup's MFMA phases overlap the other's softmax;
 //  * both contractions run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
 //    Scores are formed transposed, S^T = K Q^T, so that each lane ends up
 //    holding one query row: its row statistics stay in-lane and the score
 //    registers, exponentiated and rounded to bf16, are directly the B operand
 //    of O^T = V^T P^T (both operands use the same k-slot order);
-//  * Q lives in registers for the whole key loop (B.2 step (1));
+//  * Q lives in registers for the whole key loop (B.2 step (1)); the paired
+//    kernel keeps both units' Q in LDS instead;
 //  * K_{j+1} is requested into registers before S_j is computed and written
-//    to the (row-padded) K tile in LDS once every wave is done with K_j;
+//    to the (row-padded) K tile in LDS once every wave is done with K_j, before
+//    V_j is requested;
 //  * V_j is requested only after tile j passed its gate; its loads overlap
 //    the softmax of the tile, then it is written to LDS.  The A operand of
 //    O^T = V^T P^T needs V transposed: it is read with ds_read_b64_tr_b16,
