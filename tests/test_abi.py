@@ -147,3 +147,15 @@ def test_calibrate_levels_rejects_before_any_launch(lib):
     assert f(good, 1, 4, 20000, 1, pks, 3, good, None) == 3     # M beyond the calibration kernel
     assert f(good + 2, 1, 4, 8, 1, pks, 3, good, None) == 4     # misaligned tile maxima
     assert f(good, 1, 4, 8, 2, pks, 3, good, None) == 2         # causal flag
+
+
+def test_missing_library_raises_and_nothing_falls_back(monkeypatch, tmp_path):
+    # with the shared library absent every entry point must fail loudly: there is no CPU path
+    monkeypatch.setattr(bb, "LIB_PATH", str(tmp_path / "absent" / "libbsfa.so"))
+    monkeypatch.setattr(bb, "_lib", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        bb.load_library()
+    with pytest.raises(RuntimeError):
+        bb.bsfa_validate(S(), 1, bb.make_block(128))
+    with pytest.raises(RuntimeError):
+        bb.status_string(0)
