@@ -108,6 +108,51 @@ __device__ __forceinline__ int v_swz(int row) {
   return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 
+// Cross-lane reductions in the VALU (no LDS round trip).  Lanes l and l ^ 32
+// hold the two halves of one score row; v_permlane32_swap exchanges lanes 32-63
+// of its first operand with lanes 0-31 of its second, v_permlane16_swap the odd
+// 16-lane rows of the first with the even rows of the second.  Applied to a
+// value and a copy of it, the first result holds the lower lanes (rows) twice
+// and the second the upper ones.  The swaps are written in inline asm: through
+// the builtins the compiler folds a maximum of the two results into the first
+// one alone.  Each asm block makes the copy itself and waits the two cycles a
+// VALU write needs before a permlane instruction reads the register.
+__device__ __forceinline__ void swap_halves(float x, float& lo, float& hi) {
+  unsigned a = __builtin_bit_cast(unsigned, x), b;
+  asm volatile("v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "=&v"(b));
+  lo = __builtin_bit_cast(float, a);
+  hi = __builtin_bit_cast(float, b);
+}
+__device__ __forceinline__ void swap_rows(float x, float& even, float& odd) {
+  unsigned a = __builtin_bit_cast(unsigned, x), b;
+  asm volatile("v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "=&v"(b));
+  even = __builtin_bit_cast(float, a);
+  odd = __builtin_bit_cast(float, b);
+}
+// max / sum over lanes l and l ^ 32
+__device__ __forceinline__ float max_halves(float x) {
+  float a, b;
+  swap_halves(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  float a, b;
+  swap_halves(x, a, b);
+  return a + b;
+}
+// Maximum over the wave of a value that already agrees between lanes l and
+// l ^ 32: within each 16-lane row by DPP (lane ^ 1, lane ^ 2, rotations by 4
+// and 8), then across rows by v_permlane16_swap.
+__device__ __forceinline__ float wave_max_sym(float x) {
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xF, 0xF, false)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false)));
+  float e, o;
+  swap_rows(x, e, o);
+  return fmaxf(e, o);
+}
+
 // Workgroup barrier that orders LDS accesses only: global loads issued before
 // it stay in flight.
 __device__ __forceinline__ void lds_barrier() {
@@ -350,10 +395,8 @@ __global__ void __launch_bounds__(BM * 2) bsfa_fwd_kernel(const FwdParams p) {
         rm1 = fmaxf(rm1, s[kb][r + 1]);
       }
     float rm = fmaxf(rm0, rm1);
-    rm = fmaxf(rm, __shfl_xor(rm, 32));  // full row max of query qloc
-    float wm = rm;
-#pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) wm = fmaxf(wm, __shfl_xor(wm, off));
+    rm = max_halves(rm);  // full row max of query qloc
+    const float wm = wave_max_sym(rm);
     if (lane == 0) red[w] = wm;
     lds_barrier();  // (b): every wave is done with K_j; red complete
     float tm = red[0];
@@ -459,8 +502,8 @@ __global__ void __launch_bounds__(BM * 2) bsfa_fwd_kernel(const FwdParams p) {
     return;
   }
   // ---- (a9) epilogue: O_i = O_acc / l, lse, skip count -------------------
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.f / (lb_run + __shfl_xor(lb_run, 32));
+  const float l_tot = sum_halves(l_run);
+  const float inv = 1.f / sum_halves(lb_run);
   if (!RAGGED || qrow < n_seq) {
     store_out_row(p, q_head + qrow, o, inv, hh);
     if (p.lse && hh == 0) p.lse[q_head + qrow] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
@@ -690,11 +733,9 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
           rm1 = fmaxf(rm1, s[kb][r + 1]);
         }
       float rm = fmaxf(rm0, rm1);
-      rm = fmaxf(rm, __shfl_xor(rm, 32));
+      rm = max_halves(rm);
       rm_t[t] = rm;
-      float wm = rm;
-#pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) wm = fmaxf(wm, __shfl_xor(wm, off));
+      const float wm = wave_max_sym(rm);
       if (lane == 0) red[u][wu][t] = wm;
     }
     lds_barrier();  // (b): every wave is done with K_js; maxima complete
@@ -841,8 +882,8 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
     return;
   }
   // ---- (a9) epilogue -------------------------------------------------------
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.f / (lb_run + __shfl_xor(lb_run, 32));
+  const float l_tot = sum_halves(l_run);
+  const float inv = 1.f / sum_halves(lb_run);
   if (!RAGGED || qrow < n_seq) {
     store_out_row(p, q_head + qrow, o, inv, hh);
     if (p.lse && hh == 0) p.lse[q_head + qrow] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
