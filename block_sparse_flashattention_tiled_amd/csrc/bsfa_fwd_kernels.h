@@ -693,6 +693,14 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
     const int c = tid + P2::NT * it;
     *reinterpret_cast<u32x4*>(k_lds + (c / C::CPR) * C::KS + (c % C::CPR) * 16) = kreg[it];
   }
+  lds_barrier();  // K_0 and Q visible
+
+  // Two barriers per step.  (b) follows S_js: every wave is done with K_js, so
+  // K_{js+1} may be stored, and (by program order) with the previous step's
+  // P.V, so V_js may be stored after the softmax.  (c) follows the V store and
+  // is taken even when no unit keeps the step: it publishes V_js and K_{js+1}
+  // and separates this step's reads of the tile maxima from the next step's
+  // writes.
 
   // One step: key tiles SUB*js .. SUB*js + SUB - 1.  DIAGC is true only for the
   // causal diagonal step(s), the last visited, so the masking of keys after the
@@ -700,7 +708,6 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
   // every other step.
   auto step = [&](const int js, auto DIAGC) {
     constexpr bool DIAG_TILE = decltype(DIAGC)::value;
-    lds_barrier();  // (a): K_js (and Q) visible; every wave is done with V_{js-1}
     // causal: a step before the diagonal always has a successor; with one
     // diagonal step it is the last
     const bool more = CAUSAL ? (!DIAG_TILE || (C::ND > 1 && js < send)) : (js < send);
@@ -841,7 +848,9 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
         if (SUB == 1 || ((vmask >> ((it * RPI) / BN)) & 1))
           *reinterpret_cast<u32x4*>(v_lds + row * (2 * D) + ((c % C::CPR) ^ v_swz<D>(row)) * 16) = vreg[it];
       }
-      lds_barrier();  // (c): V of the step's kept tiles complete
+    }
+    lds_barrier();  // (c): V of the step's kept tiles and K_{js+1} complete
+    if (vmask) {
       if (kmask) {
 #pragma unroll
         for (int kc = 0; kc < C::PC; ++kc) {
