@@ -24,7 +24,11 @@ Also reported, outside ``value``:
   * ``tile_study``: on the same inputs, the sweep on 128 x 64 tiles (the
     pages' A100 tile: finer skip granularity, half the work per gate) next
     to 128 x 128 - skip fraction, time and error against the dense output
-    (``--no-tile-study`` skips it).
+    (``--no-tile-study`` skips it);
+  * ``cold_cache``: each sweep point timed right after a 512 MB buffer has
+    been overwritten on the same stream, so that no K/V tile is left in L2 or
+    the Infinity Cache when the launch starts (``--no-cold-cache`` skips it);
+  * ``device``: the GPU's name and compute-unit count as the runtime reports them.
 
 Prints one JSON line.  ``--gpus N`` with N > 1 exits: this build runs on one GPU.
 """
@@ -207,6 +211,29 @@ class Layer:
             pt["dense_equivalent_tflops"] = dense_flops / (pt["ms_mean"] * 1e-3) / 1e12
         return total_ms / steps
 
+    def measure_cold(self, points, reps, flush_bytes=512 << 20):
+        """Mean launch time of each point when the launch follows an overwrite of
+        ``flush_bytes`` of device memory (caches hold no K/V tile of the layer)."""
+        torch, w = self.torch, self.w
+        buf = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+        counts = torch.empty((w.batch, w.heads_q, self.M), dtype=torch.int32, device="cuda")
+        out = []
+        for pt in points:
+            durs = []
+            for r in range(reps + 1):  # the first launch of a point is not counted
+                buf.fill_(float(r))
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(self.stream)
+                self.launch(pt, counts)
+                e1.record(self.stream)
+                torch.cuda.synchronize()
+                if r:
+                    durs.append(e0.elapsed_time(e1))
+            out.append({"target": pt["target"], "k": pt["k"], "ms_cold_mean": float(np.mean(durs)),
+                        "ms_warm_mean": pt["ms_mean"], "cold_over_warm": float(np.mean(durs)) / pt["ms_mean"]})
+        del buf
+        return out
+
     def errors_vs(self, ref_out, ref_lse, pt):
         """Error of one point's output against a reference output (same inputs)."""
         torch, w = self.torch, self.w
@@ -245,6 +272,7 @@ def main():
     ap.add_argument("--no-128k", action="store_true", help="skip the 128K long-context leg")
     ap.add_argument("--no-gate-study", action="store_true", help="skip the gap-gate comparison")
     ap.add_argument("--no-tile-study", action="store_true", help="skip the 128 x 64 tile comparison")
+    ap.add_argument("--no-cold-cache", action="store_true", help="skip the cold-cache timing of the sweep")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="also run one plain 1 GiB device copy, whose HBM counters calibrate the kernel's")
     args = ap.parse_args()
@@ -326,6 +354,14 @@ def main():
             "traffic": measured_traffic(w.name),
         },
     }
+    props = torch.cuda.get_device_properties(0)
+    res["device"] = {"name": props.name, "compute_units": props.multi_processor_count,
+                     "arch": getattr(props, "gcnArchName", None)}
+    if not args.no_cold_cache:
+        res["cold_cache"] = {
+            "flush": "512 MB device buffer overwritten on the launch stream before each timed launch",
+            "points": lay.measure_cold(points, 3),
+        }
 
     # ---- the dense output: reference of both studies --------------------------
     if not (args.no_gate_study and args.no_tile_study):
