@@ -129,9 +129,11 @@ def _plant(q_bits, k_bits, b, g, group, count, lo, rng, taken):
     """Plant ``count`` keys K[b,g,kpos] = 4*Q[b,h,qpos] with kpos <= qpos.
 
     Multiplying a bfloat16 value by 4 only moves its exponent, so the planted
-    key is exactly representable.  Key positions are distinct and >= ``lo``.
+    key is exactly representable.  Key positions are distinct and >= ``lo``; a
+    sequence with fewer free positions than ``count`` gets one per free position.
     """
     n = q_bits.shape[2]
+    count = min(count, max(0, n - lo - sum(1 for t in taken if t >= lo)))
     planted = []
     while len(planted) < count:
         h = g * group + int(rng.integers(group))

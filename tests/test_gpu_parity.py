@@ -67,6 +67,12 @@ CASES = {
     "ragged-single-partial-tile": (dict(base="llama8k", seq_len=77, heads_q=2, heads_kv=1), None, "+inf"),
     "ragged-dense-bidirectional": (dict(base="llama8k", seq_len=333, heads_q=2, heads_kv=2, causal=False), None,
                                    "calib"),
+    # degenerate shapes: a single token (one partial block, only the diagonal tile), and a threshold table
+    # longer than the number of query blocks (entries past the last block are never read)
+    "single-token-causal": (dict(base="llama8k", seq_len=1, heads_q=2, heads_kv=1), 3, "calib"),
+    "single-token-bidirectional-d64": (dict(base="tiny", seq_len=1, heads_q=2, heads_kv=1, causal=False), 3,
+                                       "calib"),
+    "table-longer-than-M": (dict(base="llama8k", seq_len=1024, heads_q=4, heads_kv=2), 3, "t_long"),
 }
 
 
@@ -83,6 +89,10 @@ def _make(name):
         # one value per head: the median of the finite per-block thresholds, kept away from every s_max
         thr = np.array([[np.median(r[np.isfinite(r)])] for r in full], dtype=np.float32)
         thr = _nudge(tm, thr)
+    elif mode == "t_long":
+        full = margin_thresholds(tm, k, w.causal)
+        # entries past the last query block: -inf would keep every tile if they were read
+        thr = np.ascontiguousarray(np.concatenate([full, np.full((w.heads_q, 5), -np.inf, np.float32)], axis=1))
     elif mode == "t_len4":
         full = margin_thresholds(tm, k, w.causal)
         thr = _nudge(tm, np.ascontiguousarray(full[:, 6:10]))  # entries of blocks 6..9, reused past the table

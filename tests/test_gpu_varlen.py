@@ -106,3 +106,31 @@ def test_varlen_matches_oracle_and_single_sequences(name):
         skipped += int(gb["skip_counts"].sum())
         print(f"[varlen {name}] b={b} n={n} {stats}", flush=True)
     assert skipped > 0
+
+
+def test_varlen_writes_nothing_past_each_sequence():
+    # outputs start as sentinels: rows past a sequence's end, counts of query blocks past its last block, and
+    # everything of an empty sequence must keep them
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    bb.load_library()
+    over, lens, k = CASES["one-unit-with-empty"]
+    over = dict(over)
+    w = wl.get_config(over.pop("base"), **over)
+    data = wl.generate(w, seed=0)
+    thr = _thresholds(data, lens, w, k)
+    q, kk, v = (bb.bits_to_device(data[n]) for n in ("q", "k", "v"))
+    B, H, N, d = w.batch, w.heads_q, w.seq_len, w.head_dim
+    M = w.n_blocks
+    out = torch.full((B, H, N, d), 1234.5, dtype=torch.float32, device="cuda")
+    lse = torch.full((B, H, N), -777.0, dtype=torch.float32, device="cuda")
+    counts = torch.full((B, H, M), -5, dtype=torch.int32, device="cuda")
+    shape = bb.make_shape(B, H, w.heads_kv, N, d, thr.shape[1])
+    bb.bsfa_prefill_varlen(q, kk, v, out, lse, counts, torch.from_numpy(thr).cuda(), shape, int(w.causal),
+                           bb.make_block(w.block), torch.tensor(lens, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    o, l, c = out.cpu().numpy(), lse.cpu().numpy(), counts.cpu().numpy()
+    for b, n in enumerate(lens):
+        Mb = -(-n // w.block)
+        assert (o[b, :, n:] == np.float32(1234.5)).all() and (l[b, :, n:] == np.float32(-777.0)).all()
+        assert (c[b, :, Mb:] == -5).all()
+        assert np.isfinite(o[b, :, :n]).all() and (c[b, :, :Mb] >= 0).all()

@@ -75,3 +75,14 @@ def test_unaligned_length_has_a_partial_last_block():
     d = wl.generate(w, seed=0)
     assert w.n_blocks == 16 and d["q"].shape[2] == 1000
     assert all(0 <= kp <= qp < 1000 for _, _, qp, kp in d["planted"])
+
+
+@pytest.mark.parametrize("n", [1, 3, 8])
+def test_sequence_shorter_than_the_needle_count(n):
+    # eight needles want eight distinct key positions; a shorter sequence gets one per position and the
+    # generator still ends
+    w = wl.get_config("tiny", seq_len=n, causal=False)
+    d = wl.generate(w, seed=0)
+    kpos = [p[3] for p in d["planted"]]
+    assert len(kpos) == min(8, n) and len(set(kpos)) == len(kpos)
+    assert all(0 <= kp <= qp < n for _, _, qp, kp in d["planted"])
