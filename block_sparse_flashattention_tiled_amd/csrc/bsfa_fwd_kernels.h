@@ -29,13 +29,16 @@
 //    holding one query row: its row statistics stay in-lane and the score
 //    registers, exponentiated and rounded to bf16, are directly the B operand
 //    of O^T = V^T P^T (both operands use the same k-slot order);
-//  * Q lives in registers for the whole key loop (B.2 step (1)); the paired
-//    kernel keeps both units' Q in LDS instead;
-//  * K_{j+1} is requested into registers before S_j is computed and written
-//    to the (row-padded) K tile in LDS once every wave is done with K_j, before
-//    V_j is requested;
+//  * Q lives in registers for the whole key loop (B.2 step (1)), in both
+//    kernels;
+//  * one-unit kernel: K_{j+1} is requested into registers before S_j is
+//    computed and written to the (row-padded) K tile in LDS once every wave is
+//    done with K_j, before V_j is requested.  Paired kernel: K_{j+1} goes
+//    straight from memory into the second of two K tiles in LDS (direct-to-LDS
+//    loads), requested before S_j, so it has a whole step to land;
 //  * V_j is requested only after tile j passed its gate; its loads overlap
-//    the softmax of the tile, then it is written to LDS.  The A operand of
+//    the softmax of the tile (one-unit kernel: into registers, then written to
+//    LDS; paired kernel: straight into LDS).  The A operand of
 //    O^T = V^T P^T needs V transposed: it is read with ds_read_b64_tr_b16,
 //    whose 16-lane groups return a 4x16 block transposed.  The V tile is
 //    XOR-swizzled so those reads are bank-conflict free;
@@ -45,7 +48,9 @@
 //  * the running output is rescaled lazily: only when a row maximum grows by
 //    more than 2^4 (exact: O and l always refer to the same reference max),
 //    and l sums the bf16-rounded P~ that multiplies V;
-//  * barriers fence LDS only, so outstanding global loads stay in flight;
+//  * barriers fence LDS only, so outstanding global loads stay in flight; the
+//    paired kernel's barrier does not wait for direct-to-LDS loads either: a
+//    wave waits for its own before the barrier that publishes the tile;
 //  * workgroups are ordered heaviest query block first (causal) and, when the
 //    grid allows, remapped so that the query heads of one KV group run back
 //    to back on the same XCD and share K_j/V_j in that XCD's L2.
@@ -520,9 +525,10 @@ __global__ void __launch_bounds__(BM * 2) bsfa_fwd_kernel(const FwdParams p) {
 // ---------------------------------------------------------------------------
 // Paired variant: one workgroup of 2*B_M/32 waves runs two query units that
 // read the same K/V stream - two query heads of one KV group on the same query
-// block, or (bidirectional) two neighbouring query blocks of one head.  Q of
-// both units sits in LDS, so a wave needs no Q registers and two waves fit on
-// each SIMD; K_j is loaded once for both units.  Each unit keeps its own gate,
+// block, or (bidirectional) two neighbouring query blocks of one head.  Two
+// waves share each SIMD; every wave keeps its 32 rows of Q in registers, and
+// K_j is loaded once for both units, straight into LDS, one step ahead into
+// the second of two K tiles.  Each unit keeps its own gate,
 // statistics and output; V_j is requested when at least one unit keeps tile j
 // and a unit that skipped the tile neither reads it nor updates anything.
 // ---------------------------------------------------------------------------
@@ -532,29 +538,49 @@ struct PairCfg {
   static constexpr int NWU = BM / 32;               // waves per unit
   static constexpr int NW = 2 * NWU;                // waves per workgroup
   static constexpr int NT = NW * 64;                // threads per workgroup
-  static constexpr int LD = C::TILE_CHUNKS / NT;    // 16-byte chunks per thread per K / V tile
-  static constexpr int QLD = BM * C::CPR / NT;      // 16-byte chunks per thread per Q tile
-  static constexpr int Q_BYTES = BM * C::KS;        // Q tile, rows padded like K
-  static_assert(LD * NT == C::TILE_CHUNKS && QLD * NT == BM * C::CPR, "loads split evenly");
 };
 
-// S^T = K_j Q^T with the Q fragments read from LDS.
-template <int D, int BM, int BN, int NKB>
-__device__ __forceinline__ void qk_tile_qlds(f32x16 (&s)[NKB], const char* ks, int k_lane, const char* qs,
-                                             int q_lane) {
+// Chunk swizzle of a dense K tile in LDS (2D bytes per row): logical 16-byte
+// chunk cc of row `row` sits at position cc ^ k_swz(row), so that 16
+// consecutive rows read at one logical chunk hit distinct banks.
+template <int D>
+__device__ __forceinline__ int k_swz(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+
+// Workgroup barrier over the LDS accesses of LDS instructions (lgkmcnt):
+// direct-to-LDS loads stay in flight across it.  The memory clobber keeps the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier_keep_dma() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Wait until this wave's vector-memory operations, direct-to-LDS loads
+// included, have completed (vmcnt(0); the LDS and export counters untouched).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// S^T = K Q^T with this wave's Q fragments in registers and K from a dense,
+// swizzled tile.
+template <int D, int BM, int BN, int NKB, int NKC>
+__device__ __forceinline__ void qk_tile_swz(f32x16 (&s)[NKB], const char* ks, int l32, int hh,
+                                            const bf16x8 (&qf)[NKC]) {
   using C = Cfg<D, BM, BN>;
-  static_assert(NKB == C::KB, "fragment size");
+  static_assert(NKB == C::KB && NKC == C::KC, "fragment sizes");
+  // Chunk 2c + hh of row l32 (rows kb*32 + l32 share the swizzle x) sits at
+  // byte l32 2D + ((2c + hh) ^ x) 16 = bx ^ 32c: the row, the bit of hh and
+  // the bits of c occupy disjoint address bits.  bx is made opaque so that
+  // the eight addresses are formed at each use rather than held in registers.
+  const int x = k_swz<D>(l32);
+  int bx = l32 * (2 * D) + ((hh ^ (x & 1)) << 4) + ((x & ~1) << 4);
+  asm volatile("" : "+v"(bx));
 #pragma unroll
   for (int kb = 0; kb < C::KB; ++kb) s[kb] = f32x16{};
 #pragma unroll
   for (int c = 0; c < C::KC; ++c) {
-    const bf16x8 qb = *reinterpret_cast<const bf16x8*>(qs + q_lane + c * 32);
+    const char* kc = ks + (bx ^ (c << 5));
     bf16x8 a[C::KB];
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-      a[kb] = *reinterpret_cast<const bf16x8*>(ks + k_lane + kb * 32 * C::KS + c * 32);
+    for (int kb = 0; kb < C::KB; ++kb) a[kb] = *reinterpret_cast<const bf16x8*>(kc + kb * 32 * 2 * D);
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], qb, s[kb], 0, 0, 0);
+    for (int kb = 0; kb < C::KB; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], qf[c], s[kb], 0, 0, 0);
   }
 }
 
@@ -572,12 +598,17 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
   using P2 = PairCfg<D, BM, KN>;
   constexpr int KBS = C::KB / SUB;      // 32-key sub-blocks per key tile
   constexpr int PCS = C::PC / SUB;      // 16-key P.V chunks per key tile
-  constexpr int RPI = P2::NT / C::CPR;  // K / V rows per load iteration
-  static_assert(BN % RPI == 0 || SUB == 1, "a V load iteration stays inside one key tile");
   static_assert(HEADPAIR || !CAUSAL, "block pairs are for bidirectional attention");
-  __shared__ __attribute__((aligned(16))) char q_lds[2][P2::Q_BYTES];
-  __shared__ __attribute__((aligned(16))) char k_lds[C::K_BYTES];
-  __shared__ __attribute__((aligned(16))) char v_lds[C::V_BYTES];
+  static_assert(C::ND == 1, "the causal diagonal fills one step");
+  // K (two buffers) and V tiles in LDS: dense rows of 2D bytes with swizzled
+  // 16-byte chunks, filled by direct-to-LDS loads of 1 KB per instruction
+  constexpr int TILE_BYTES = KN * D * 2;
+  constexpr int DMA = TILE_BYTES / (P2::NW * 1024);  // load instructions per wave and tile
+  static_assert(DMA * P2::NW * 1024 == TILE_BYTES, "tile loads split evenly over the waves");
+  static_assert(SUB == 1 || BN % (64 / C::CPR) == 0, "a load instruction stays inside one key tile");
+  __shared__ __attribute__((aligned(16))) char k_lds0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char k_lds1[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char v_lds[TILE_BYTES];
   __shared__ float red[2][P2::NWU][SUB];
 
   const int tid = threadIdx.x;
@@ -627,30 +658,18 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
   const size_t kv_head = (size_t)(b * p.Hkv + g) * p.N;
   const int qloc = 32 * wu + l32;
   const int qrow = i * BM + qloc;
-  constexpr int TILE_CHUNKS = C::TILE_CHUNKS;
-
-  const int k_lane = l32 * C::KS + hh * 16;
-  const int q_lane = qloc * C::KS + hh * 16;
   const int v_row = 4 * hh + ((lane & 15) >> 2);
   const int v_col = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int v_half = (lane & 1) * 8;
 
-  // ---- (a2) Q of both units -> LDS ------------------------------------------
+  // ---- (a2) Q: this wave's 32 rows stay in registers as MFMA B fragments ------
+  // (a row past the end of the sequence reads the last row; it is masked)
+  bf16x8 qf[C::KC];
+  {
+    const int qr = RAGGED ? min(qrow, n_seq - 1) : qrow;
+    const bf16x8* qsrc = reinterpret_cast<const bf16x8*>(p.q) + (q_head + qr) * (D / 8) + hh;
 #pragma unroll
-  for (int uu = 0; uu < 2; ++uu) {
-    const u32x4* qh = reinterpret_cast<const u32x4*>(p.q) + (size_t)(b * p.Hq + hq_u[uu]) * p.N * C::CPR;
-    const u32x4* qg = qh + (size_t)i_u[uu] * BM * C::CPR;
-    u32x4 qr[P2::QLD];
-#pragma unroll
-    for (int it = 0; it < P2::QLD; ++it) {
-      const int c = tid + P2::NT * it;
-      qr[it] = RAGGED ? qh[tile_chunk<C::CPR>(i_u[uu] * BM, c, n_seq)] : qg[c];
-    }
-#pragma unroll
-    for (int it = 0; it < P2::QLD; ++it) {
-      const int c = tid + P2::NT * it;
-      *reinterpret_cast<u32x4*>(q_lds[uu] + (c / C::CPR) * C::KS + (c % C::CPR) * 16) = qr[it];
-    }
+    for (int c = 0; c < C::KC; ++c) qf[c] = qsrc[2 * c];
   }
   const u32x4* kg = reinterpret_cast<const u32x4*>(p.k) + kv_head * C::CPR;
   const u32x4* vg = reinterpret_cast<const u32x4*>(p.v) + kv_head * C::CPR;
@@ -681,47 +700,65 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
   float mrun_u[2] = {-INFINITY, -INFINITY};  // per unit: largest s_max of its kept tiles (gap gate)
   int nskip = 0;
 
-  u32x4 kreg[P2::LD];
-  u32x4 vreg[P2::LD];
+  // Direct-to-LDS load of the K or V tile of the step whose first key is row0:
+  // instruction n of wave w fills the 1 KB of chunks (w DMA + n) 64 .. + 63,
+  // lane l the chunk at position l of them, with the logical chunk that the
+  // swizzle puts there.  tmask: the step's key tiles to load.
+  const int ws = __builtin_amdgcn_readfirstlane(w);
+  // Addresses: the tile's first row (uniform) plus a 32-bit lane offset.
+  auto dma_tile = [&](char* dst, const u32x4* head, int row0, bool is_k, int tmask) {
+    const char* base = reinterpret_cast<const char*>(head + (size_t)row0 * C::CPR);
+    // with tails, the lane offsets are formed here at each call rather than
+    // kept across the loop (registers)
+    int ln = lane;
+    if constexpr (RAGGED) asm volatile("" : "+v"(ln));
 #pragma unroll
-  for (int it = 0; it < P2::LD; ++it) {
-    const int c = tid + P2::NT * it;
-    kreg[it] = kg[RAGGED ? tile_chunk<C::CPR>(0, c, n_seq) : c];
-  }
-#pragma unroll
-  for (int it = 0; it < P2::LD; ++it) {
-    const int c = tid + P2::NT * it;
-    *reinterpret_cast<u32x4*>(k_lds + (c / C::CPR) * C::KS + (c % C::CPR) * 16) = kreg[it];
-  }
-  lds_barrier();  // K_0 and Q visible
+    for (int n = 0; n < DMA; ++n) {
+      const int chunk0 = (ws * DMA + n) * 64;
+      if (SUB > 1 && !((tmask >> ((chunk0 / C::CPR) / BN)) & 1)) continue;
+      const int slot = chunk0 + ln;
+      const int row = slot / C::CPR;
+      const int cc = (slot % C::CPR) ^ (is_k ? k_swz<D>(row) : v_swz<D>(row));
+      const int rrow = RAGGED ? min(row, n_seq - 1 - row0) : row;  // rows past the end read the last row
+      const unsigned off = (unsigned)(rrow * C::CPR + cc) * 16u;
+      __builtin_amdgcn_global_load_lds((const void*)(base + off),
+                                       (__attribute__((address_space(3))) void*)(dst + chunk0 * 16), 16, 0, 0);
+    }
+  };
+  // K_js lives in buffer (js + par) & 1, so that the last step reads k_lds0
+  // and every buffer choice is known at compile time
+  const int par = send & 1;
+  if (par) dma_tile(k_lds1, kg, 0, true, (1 << SUB) - 1);
+  else dma_tile(k_lds0, kg, 0, true, (1 << SUB) - 1);
+  wait_vmem();
+  lds_barrier_keep_dma();  // K_0 visible
 
-  // Two barriers per step.  (b) follows S_js: every wave is done with K_js, so
-  // K_{js+1} may be stored, and (by program order) with the previous step's
-  // P.V, so V_js may be stored after the softmax.  (c) follows the V store and
-  // is taken even when no unit keeps the step: it publishes V_js and K_{js+1}
-  // and separates this step's reads of the tile maxima from the next step's
-  // writes.
+  // Two barriers per step.  (b) follows S_js: the tile maxima are complete and
+  // (by program order) every wave is done with the previous step's P.V, so
+  // V_js may be loaded into LDS.  K_{js+1} needs no barrier of its own: it goes
+  // into the other K tile, whose last reader, S_{js-1}, came before the
+  // previous step's (b).  (c) follows each wave's wait for its own V_js and
+  // K_{js+1} loads and is taken even when no unit keeps the step: it publishes
+  // both and separates this step's reads of the tile maxima from the next
+  // step's writes.
 
   // One step: key tiles SUB*js .. SUB*js + SUB - 1.  DIAGC is true only for the
-  // causal diagonal step(s), the last visited, so the masking of keys after the
+  // causal diagonal step, the last visited, so the masking of keys after the
   // query is compiled into those steps and not evaluated (or predicated) on
   // every other step.
-  auto step = [&](const int js, auto DIAGC) {
+  auto step = [&](const int js, auto DIAGC, auto KBUF) {
     constexpr bool DIAG_TILE = decltype(DIAGC)::value;
-    // causal: a step before the diagonal always has a successor; with one
-    // diagonal step it is the last
-    const bool more = CAUSAL ? (!DIAG_TILE || (C::ND > 1 && js < send)) : (js < send);
-    if (more) {
-      const u32x4* src = kg + (size_t)(js + 1) * TILE_CHUNKS;
-#pragma unroll
-      for (int it = 0; it < P2::LD; ++it) {
-        const int c = tid + P2::NT * it;
-        kreg[it] = RAGGED ? kg[tile_chunk<C::CPR>((js + 1) * KN, c, n_seq)] : src[c];
-      }
-    }
+    char* const k_cur = decltype(KBUF)::value ? k_lds1 : k_lds0;  // K_js
+    char* const k_nxt = decltype(KBUF)::value ? k_lds0 : k_lds1;  // K_{js+1}
+    // causal: a step before the diagonal always has a successor; the diagonal
+    // step is the last
+    const bool more = CAUSAL ? !DIAG_TILE : (js < send);
+    // K_{js+1} -> the other buffer; its last reader, S_{js-1}, finished
+    // before barrier (b) of the previous step
+    if (more) dma_tile(k_nxt, kg, (js + 1) * KN, true, (1 << SUB) - 1);
     // ---- (a4) S^T = K Q^T over the step's keys -------------------------------
     f32x16 s[C::KB];
-    qk_tile_qlds<D, BM, KN>(s, k_lds, k_lane, q_lds[u], q_lane);
+    qk_tile_swz<D, BM, KN>(s, k_cur, l32, hh, qf);
     if constexpr (CAUSAL && DIAG_TILE) mask_causal(s, qloc, hh, i * BM - js * KN);
     if constexpr (RAGGED) {
       const int rows_left = n_seq - i * BM, keys_left = n_seq - js * KN;
@@ -745,7 +782,7 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
       const float wm = wave_max_sym(rm);
       if (lane == 0) red[u][wu][t] = wm;
     }
-    lds_barrier();  // (b): every wave is done with K_js; maxima complete
+    lds_barrier_keep_dma();  // (b): maxima complete; every wave is done with P.V of the previous step
     // gates in increasing key-tile order (the gap gate's running maximum)
     int skip_of[2][SUB];
 #pragma unroll
@@ -777,26 +814,8 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
     const int kmask = __builtin_amdgcn_readfirstlane(km);
     const int vmask = __builtin_amdgcn_readfirstlane(vm);
     nskip += ns;  // (a6)
-    // K_{j+1} -> LDS before V_j is requested: vector loads complete in issue
-    // order, so waiting for K_{j+1} after the V_j requests would also wait for
-    // V_j, whose latency is meant to hide behind the softmax
-    if (more) {
-#pragma unroll
-      for (int it = 0; it < P2::LD; ++it) {
-        const int c = tid + P2::NT * it;
-        *reinterpret_cast<u32x4*>(k_lds + (c / C::CPR) * C::KS + (c % C::CPR) * 16) = kreg[it];
-      }
-    }
-    // ---- (a8) V of a key tile requested only if some unit keeps the tile -----
-    if (vmask) {
-      const u32x4* src = vg + (size_t)js * TILE_CHUNKS;
-#pragma unroll
-      for (int it = 0; it < P2::LD; ++it) {
-        const int c = tid + P2::NT * it;
-        if (SUB == 1 || ((vmask >> ((it * RPI) / BN)) & 1))
-          vreg[it] = RAGGED ? vg[tile_chunk<C::CPR>(js * KN, c, n_seq)] : src[c];
-      }
-    }
+    // ---- (a8) V of the step's key tiles that some unit keeps -> LDS -----------
+    if (vmask) dma_tile(v_lds, vg, js * KN, false, vmask);
     bf16x8 pf[C::PC];
     if (kmask) {
       // ---- (a7) online softmax over the kept key tiles (lazy rescale, see the
@@ -840,16 +859,8 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
       l_run += rs0 + rs1;
       lb_run += rb0 + rb1;
     }
-    if (vmask) {
-#pragma unroll
-      for (int it = 0; it < P2::LD; ++it) {
-        const int c = tid + P2::NT * it;
-        const int row = c / C::CPR;
-        if (SUB == 1 || ((vmask >> ((it * RPI) / BN)) & 1))
-          *reinterpret_cast<u32x4*>(v_lds + row * (2 * D) + ((c % C::CPR) ^ v_swz<D>(row)) * 16) = vreg[it];
-      }
-    }
-    lds_barrier();  // (c): V of the step's kept tiles and K_{js+1} complete
+    wait_vmem();             // this wave's loads of V_js and K_{js+1} have landed
+    lds_barrier_keep_dma();  // (c): V of the step's kept tiles and K_{js+1} complete
     if (vmask) {
       if (kmask) {
 #pragma unroll
@@ -869,19 +880,15 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
       }
     }
   };
-  if constexpr (CAUSAL) {
-    // the steps holding diagonal tiles come last; with SUB > 1 the diagonal
-    // tiles of a query block fill exactly one step
-    const int sd0 = jd0_u[0] / SUB;
-    for (int js = 0; js < sd0; ++js) step(js, std::false_type{});
-    if constexpr (C::ND == 1) {
-      step(send, std::true_type{});  // the only diagonal step: sd0 == send
-    } else {
-      for (int js = sd0; js <= send; ++js) step(js, std::true_type{});
-    }
-  } else {
-    for (int js = 0; js <= send; ++js) step(js, std::false_type{});
+  // Steps before the last in pairs (K in buffers 0, 1; a leading odd step in
+  // buffer 1); the last step, the causal diagonal, reads buffer 0.
+  using KB0 = std::integral_constant<int, 0>;
+  using KB1 = std::integral_constant<int, 1>;
+  for (int js = -par; js < send; js += 2) {
+    if (js >= 0) step(js, std::false_type{}, KB0{});
+    step(js + 1, std::false_type{}, KB1{});
   }
+  step(send, std::integral_constant<bool, CAUSAL>{}, KB0{});
 
   const int utid = wu * 64 + lane;  // thread index inside the unit
   constexpr int UNT = P2::NWU * 64;
