@@ -753,12 +753,13 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
     // causal: a step before the diagonal always has a successor; the diagonal
     // step is the last
     const bool more = CAUSAL ? !DIAG_TILE : (js < send);
-    // K_{js+1} -> the other buffer; its last reader, S_{js-1}, finished
-    // before barrier (b) of the previous step
-    if (more) dma_tile(k_nxt, kg, (js + 1) * KN, true, (1 << SUB) - 1);
     // ---- (a4) S^T = K Q^T over the step's keys -------------------------------
     f32x16 s[C::KB];
     qk_tile_swz<D, BM, KN>(s, k_cur, l32, hh, qf);
+    // K_{js+1} -> the other buffer (its last reader, S_{js-1}, finished before
+    // barrier (b) of the previous step).  Issued behind the MFMAs of S_js, whose
+    // tail hides the cost of issuing the loads; they land by barrier (c).
+    if (more) dma_tile(k_nxt, kg, (js + 1) * KN, true, (1 << SUB) - 1);
     if constexpr (CAUSAL && DIAG_TILE) mask_causal(s, qloc, hh, i * BM - js * KN);
     if constexpr (RAGGED) {
       const int rows_left = n_seq - i * BM, keys_left = n_seq - js * KN;
