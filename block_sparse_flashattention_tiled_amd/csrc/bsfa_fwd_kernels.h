@@ -134,11 +134,16 @@ __device__ __forceinline__ void swap_rows(float x, float& even, float& odd) {
   even = __builtin_bit_cast(float, a);
   odd = __builtin_bit_cast(float, b);
 }
+// Maximum that propagates NaN (IEEE maximum, v_maximum3_f32 on gfx950): unlike
+// fmaxf it needs no canonicalisation of operands that come from MFMA, DPP or
+// LDS, and a NaN score makes the tile maximum NaN, as a plain max does.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // max / sum over lanes l and l ^ 32
 __device__ __forceinline__ float max_halves(float x) {
   float a, b;
   swap_halves(x, a, b);
-  return fmaxf(a, b);
+  return vmax(a, b);
 }
 __device__ __forceinline__ float sum_halves(float x) {
   float a, b;
@@ -149,13 +154,13 @@ __device__ __forceinline__ float sum_halves(float x) {
 // l ^ 32: within each 16-lane row by DPP (lane ^ 1, lane ^ 2, rotations by 4
 // and 8), then across rows by v_permlane16_swap.
 __device__ __forceinline__ float wave_max_sym(float x) {
-  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false)));
-  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false)));
-  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xF, 0xF, false)));
-  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false)));
+  x = vmax(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false)));
+  x = vmax(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false)));
+  x = vmax(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xF, 0xF, false)));
+  x = vmax(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false)));
   float e, o;
   swap_rows(x, e, o);
-  return fmaxf(e, o);
+  return vmax(e, o);
 }
 
 // Workgroup barrier that orders LDS accesses only: global loads issued before
@@ -396,17 +401,17 @@ __global__ void __launch_bounds__(BM * 2) bsfa_fwd_kernel(const FwdParams p) {
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        rm0 = fmaxf(rm0, s[kb][r]);
-        rm1 = fmaxf(rm1, s[kb][r + 1]);
+        rm0 = vmax(rm0, s[kb][r]);
+        rm1 = vmax(rm1, s[kb][r + 1]);
       }
-    float rm = fmaxf(rm0, rm1);
+    float rm = vmax(rm0, rm1);
     rm = max_halves(rm);  // full row max of query qloc
     const float wm = wave_max_sym(rm);
     if (lane == 0) red[w] = wm;
     lds_barrier();  // (b): every wave is done with K_j; red complete
     float tm = red[0];
 #pragma unroll
-    for (int ww = 1; ww < C::NW; ++ww) tm = fmaxf(tm, red[ww]);
+    for (int ww = 1; ww < C::NW; ++ww) tm = vmax(tm, red[ww]);
     const float tms = tm * p.scale;  // s_max in the scaled-score domain
     int skip = MAXONLY ? 1 : gate_skip(p.gate, !diag, tms, tau, mrun);
     skip = __builtin_amdgcn_readfirstlane(skip);
@@ -774,10 +779,10 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
       for (int kb = t * KBS; kb < (t + 1) * KBS; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          rm0 = fmaxf(rm0, s[kb][r]);
-          rm1 = fmaxf(rm1, s[kb][r + 1]);
+          rm0 = vmax(rm0, s[kb][r]);
+          rm1 = vmax(rm1, s[kb][r + 1]);
         }
-      float rm = fmaxf(rm0, rm1);
+      float rm = vmax(rm0, rm1);
       rm = max_halves(rm);
       rm_t[t] = rm;
       const float wm = wave_max_sym(rm);
@@ -794,7 +799,7 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
         const bool exists = SUB == 1 || j < mkv_seq;  // the last step may hold a tile past the end
         float tm = red[uu][0][t];
 #pragma unroll
-        for (int ww = 1; ww < P2::NWU; ++ww) tm = fmaxf(tm, red[uu][ww][t]);
+        for (int ww = 1; ww < P2::NWU; ++ww) tm = vmax(tm, red[uu][ww][t]);
         const float tms = tm * p.scale;
         const bool on_diag = j >= jd0_u[uu] && j <= jd1_u[uu];
         skip_of[uu][t] = (MAXONLY || !exists) ? 1 : gate_skip(p.gate, !on_diag, tms, tau_u[uu], mrun_u[uu]);
@@ -824,7 +829,7 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
       float rm = -INFINITY;
 #pragma unroll
       for (int t = 0; t < SUB; ++t)
-        if (SUB == 1 || ((kmask >> t) & 1)) rm = fmaxf(rm, rm_t[t]);
+        if (SUB == 1 || ((kmask >> t) & 1)) rm = vmax(rm, rm_t[t]);
       const float m_tile = rm * c2;
       const bool grow = m_tile > m_run + 4.f;
       if (__builtin_amdgcn_ballot_w64(grow)) {
