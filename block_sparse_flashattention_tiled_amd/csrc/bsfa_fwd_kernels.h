@@ -823,28 +823,13 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
     // ---- (a8) V of the step's key tiles that some unit keeps -> LDS -----------
     if (vmask) dma_tile(v_lds, vg, js * KN, false, vmask);
     bf16x8 pf[C::PC];
-    if (kmask) {
-      // ---- (a7) online softmax over the kept key tiles (lazy rescale, see the
-      // single-unit kernel) --------------------------------------------------
-      float rm = -INFINITY;
+    // ---- (a7) online softmax over the kept key tiles, in two halves of the
+    // step's keys (lazy rescale, see the single-unit kernel) ------------------
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float rs0 = 0.f, rs1 = 0.f, rb0 = 0.f, rb1 = 0.f;
+    auto softmax_half = [&](int h) {
 #pragma unroll
-      for (int t = 0; t < SUB; ++t)
-        if (SUB == 1 || ((kmask >> t) & 1)) rm = vmax(rm, rm_t[t]);
-      const float m_tile = rm * c2;
-      const bool grow = m_tile > m_run + 4.f;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float m_new = grow ? m_tile : m_run;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-        lb_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
-        m_run = m_new;
-      }
-      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-      float rs0 = 0.f, rs1 = 0.f, rb0 = 0.f, rb1 = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
+      for (int kb = h * (C::KB / 2); kb < (h + 1) * (C::KB / 2); ++kb) {
         if (SUB > 1 && !((kmask >> (kb / KBS)) & 1)) continue;
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
@@ -862,28 +847,55 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
             pf[2 * kb + hf][r + 1] = pb[1];
           }
       }
-      l_run += rs0 + rs1;
-      lb_run += rb0 + rb1;
+    };
+    // ---- (a8) P.V over one half of the step's keys ------------------------
+    auto pv_half = [&](int h) {
+#pragma unroll
+      for (int kc = h * (C::PC / 2); kc < (h + 1) * (C::PC / 2); ++kc) {
+        if (SUB > 1 && !((kmask >> (kc / PCS)) & 1)) continue;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const int row = 16 * kc + v_row;
+          const int chunk = (4 * db + v_col) ^ v_swz<D>(row);
+          const char* base = v_lds + row * (2 * D) + chunk * 16 + v_half;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * 2 * D));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kc], o[db], 0, 0, 0);
+        }
+      }
+    };
+    if (kmask) {
+      float rm = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < SUB; ++t)
+        if (SUB == 1 || ((kmask >> t) & 1)) rm = vmax(rm, rm_t[t]);
+      const float m_tile = rm * c2;
+      const bool grow = m_tile > m_run + 4.f;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? m_tile : m_run;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+        lb_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
+        m_run = m_new;
+      }
+      softmax_half(0);
     }
     wait_vmem();             // this wave's loads of V_js and K_{js+1} have landed
     lds_barrier_keep_dma();  // (c): V of the step's kept tiles and K_{js+1} complete
-    if (vmask) {
-      if (kmask) {
-#pragma unroll
-        for (int kc = 0; kc < C::PC; ++kc) {
-          if (SUB > 1 && !((kmask >> (kc / PCS)) & 1)) continue;
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db) {
-            const int row = 16 * kc + v_row;
-            const int chunk = (4 * db + v_col) ^ v_swz<D>(row);
-            const char* base = v_lds + row * (2 * D) + chunk * 16 + v_half;
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * 2 * D));
-            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kc], o[db], 0, 0, 0);
-          }
-        }
-      }
+    // The two units take the second half in opposite orders, so that one
+    // wave's P.V of the first half runs against the other wave's exponentials
+    // on the same SIMD (waves w and w + NWU share a SIMD).
+    if (kmask) {
+      const bool pv_first = __builtin_amdgcn_readfirstlane(u) == 0;
+      if (pv_first) pv_half(0);
+      softmax_half(1);
+      if (!pv_first) pv_half(0);
+      pv_half(1);
+      l_run += rs0 + rs1;
+      lb_run += rb0 + rb1;
     }
   };
   // Steps before the last in pairs (K in buffers 0, 1; a leading odd step in
