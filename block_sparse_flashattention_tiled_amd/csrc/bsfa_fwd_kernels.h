@@ -545,6 +545,13 @@ struct PairCfg {
   static constexpr int NT = NW * 64;                // threads per workgroup
 };
 
+// 16 bytes per lane from a buffer (base, size in bytes; lane and scalar byte
+// offsets) straight into LDS at dst + 16 * lane.
+__device__ __forceinline__ void buffer_load_lds16(const void* base, int bytes, char* dst, int voff, int soff) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
+}
+
 // Chunk swizzle of a dense K tile in LDS (2D bytes per row): logical 16-byte
 // chunk cc of row `row` sits at position cc ^ k_swz(row), so that 16
 // consecutive rows read at one logical chunk hit distinct banks.
@@ -710,9 +717,9 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
   // lane l the chunk at position l of them, with the logical chunk that the
   // swizzle puts there.  tmask: the step's key tiles to load.
   const int ws = __builtin_amdgcn_readfirstlane(w);
-  // Addresses: the tile's first row (uniform) plus a 32-bit lane offset.
+  // Buffer loads: the head's K or V as a buffer resource (scalar), the tile's
+  // first row as a scalar offset, the chunk as a 32-bit lane offset.
   auto dma_tile = [&](char* dst, const u32x4* head, int row0, bool is_k, int tmask) {
-    const char* base = reinterpret_cast<const char*>(head + (size_t)row0 * C::CPR);
     // with tails, the lane offsets are formed here at each call rather than
     // kept across the loop (registers)
     int ln = lane;
@@ -725,9 +732,7 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
       const int row = slot / C::CPR;
       const int cc = (slot % C::CPR) ^ (is_k ? k_swz<D>(row) : v_swz<D>(row));
       const int rrow = RAGGED ? min(row, n_seq - 1 - row0) : row;  // rows past the end read the last row
-      const unsigned off = (unsigned)(rrow * C::CPR + cc) * 16u;
-      __builtin_amdgcn_global_load_lds((const void*)(base + off),
-                                       (__attribute__((address_space(3))) void*)(dst + chunk0 * 16), 16, 0, 0);
+      buffer_load_lds16(head, p.N * D * 2, dst + chunk0 * 16, (rrow * C::CPR + cc) * 16, row0 * (C::CPR * 16));
     }
   };
   // K_js lives in buffer (js + par) & 1, so that the last step reads k_lds0
