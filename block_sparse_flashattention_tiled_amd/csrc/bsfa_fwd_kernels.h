@@ -621,7 +621,7 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
   __shared__ __attribute__((aligned(16))) char k_lds0[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char k_lds1[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char v_lds[TILE_BYTES];
-  __shared__ float red[2][P2::NWU][SUB];
+  __shared__ float red[2][2][P2::NWU][SUB];  // [step parity][unit][wave][key tile]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -742,15 +742,21 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
   else dma_tile(k_lds0, kg, 0, true, (1 << SUB) - 1);
   wait_vmem();
   lds_barrier_keep_dma();  // K_0 visible
+  // K_1 (published by barrier (b) of step 0)
+  if (send >= 1) {
+    if (par) dma_tile(k_lds0, kg, KN, true, (1 << SUB) - 1);
+    else dma_tile(k_lds1, kg, KN, true, (1 << SUB) - 1);
+  }
 
-  // Two barriers per step.  (b) follows S_js: the tile maxima are complete and
-  // (by program order) every wave is done with the previous step's P.V, so
-  // V_js may be loaded into LDS.  K_{js+1} needs no barrier of its own: it goes
-  // into the other K tile, whose last reader, S_{js-1}, came before the
-  // previous step's (b).  (c) follows each wave's wait for its own V_js and
-  // K_{js+1} loads and is taken even when no unit keeps the step: it publishes
-  // both and separates this step's reads of the tile maxima from the next
-  // step's writes.
+  // Barriers per step.  (b) follows S_js and each wave's wait for its own
+  // K_{js+1} loads: the tile maxima and K_{js+1} are complete, every wave is
+  // done with K_js (whose tile then receives K_{js+2}) and, by program order,
+  // with the previous step's P.V, so V_js may be loaded into LDS.  (c) follows
+  // each wave's wait for its V_js loads and publishes them; it is taken only
+  // when some unit keeps a tile of the step (the same decision in every wave),
+  // so a step that both units skip has one barrier.  The tile maxima are
+  // exchanged through one of two slots by step parity, so a wave that runs
+  // ahead into the next step never overwrites maxima another wave still reads.
 
   // One step: key tiles SUB*js .. SUB*js + SUB - 1.  DIAGC is true only for the
   // causal diagonal step, the last visited, so the masking of keys after the
@@ -759,17 +765,9 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
   auto step = [&](const int js, auto DIAGC, auto KBUF) {
     constexpr bool DIAG_TILE = decltype(DIAGC)::value;
     char* const k_cur = decltype(KBUF)::value ? k_lds1 : k_lds0;  // K_js
-    char* const k_nxt = decltype(KBUF)::value ? k_lds0 : k_lds1;  // K_{js+1}
-    // causal: a step before the diagonal always has a successor; the diagonal
-    // step is the last
-    const bool more = CAUSAL ? !DIAG_TILE : (js < send);
     // ---- (a4) S^T = K Q^T over the step's keys -------------------------------
     f32x16 s[C::KB];
     qk_tile_swz<D, BM, KN>(s, k_cur, l32, hh, qf);
-    // K_{js+1} -> the other buffer (its last reader, S_{js-1}, finished before
-    // barrier (b) of the previous step).  Issued behind the MFMAs of S_js, whose
-    // tail hides the cost of issuing the loads; they land by barrier (c).
-    if (more) dma_tile(k_nxt, kg, (js + 1) * KN, true, (1 << SUB) - 1);
     if constexpr (CAUSAL && DIAG_TILE) mask_causal(s, qloc, hh, i * BM - js * KN);
     if constexpr (RAGGED) {
       const int rows_left = n_seq - i * BM, keys_left = n_seq - js * KN;
@@ -791,9 +789,13 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
       rm = max_halves(rm);
       rm_t[t] = rm;
       const float wm = wave_max_sym(rm);
-      if (lane == 0) red[u][wu][t] = wm;
+      if (lane == 0) red[decltype(KBUF)::value][u][wu][t] = wm;
     }
-    lds_barrier_keep_dma();  // (b): maxima complete; every wave is done with P.V of the previous step
+    wait_vmem();             // this wave's loads of K_{js+1} have landed
+    lds_barrier_keep_dma();  // (b): maxima and K_{js+1} complete; every wave is done with S_js and
+                             // with P.V of the previous step
+    // K_{js+2} -> K_js's tile, published by barrier (b) of the next step
+    if (!(CAUSAL && DIAG_TILE) && js + 2 <= send) dma_tile(k_cur, kg, (js + 2) * KN, true, (1 << SUB) - 1);
     // gates in increasing key-tile order (the gap gate's running maximum)
     int skip_of[2][SUB];
 #pragma unroll
@@ -802,9 +804,9 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
       for (int t = 0; t < SUB; ++t) {
         const int j = js * SUB + t;
         const bool exists = SUB == 1 || j < mkv_seq;  // the last step may hold a tile past the end
-        float tm = red[uu][0][t];
+        float tm = red[decltype(KBUF)::value][uu][0][t];
 #pragma unroll
-        for (int ww = 1; ww < P2::NWU; ++ww) tm = vmax(tm, red[uu][ww][t]);
+        for (int ww = 1; ww < P2::NWU; ++ww) tm = vmax(tm, red[decltype(KBUF)::value][uu][ww][t]);
         const float tms = tm * p.scale;
         const bool on_diag = j >= jd0_u[uu] && j <= jd1_u[uu];
         skip_of[uu][t] = (MAXONLY || !exists) ? 1 : gate_skip(p.gate, !on_diag, tms, tau_u[uu], mrun_u[uu]);
@@ -888,8 +890,10 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
       }
       softmax_half(0);
     }
-    wait_vmem();             // this wave's loads of V_js and K_{js+1} have landed
-    lds_barrier_keep_dma();  // (c): V of the step's kept tiles and K_{js+1} complete
+    if (vmask) {
+      wait_vmem();             // this wave's loads of V_js have landed
+      lds_barrier_keep_dma();  // (c): V of the step's kept tiles complete
+    }
     // The two units take the second half in opposite orders, so that one
     // wave's P.V of the first half runs against the other wave's exponentials
     // on the same SIMD (waves w and w + NWU share a SIMD).
