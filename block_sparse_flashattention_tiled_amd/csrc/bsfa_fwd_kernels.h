@@ -33,9 +33,10 @@
 //    kernels;
 //  * one-unit kernel: K_{j+1} is requested into registers before S_j is
 //    computed and written to the (row-padded) K tile in LDS once every wave is
-//    done with K_j, before V_j is requested.  Paired kernel: K_{j+1} goes
-//    straight from memory into the second of two K tiles in LDS (direct-to-LDS
-//    loads), requested before S_j, so it has a whole step to land;
+//    done with K_j, before V_j is requested.  Paired kernel: K goes straight
+//    from memory into LDS (buffer loads with an LDS destination), two K tiles
+//    in turn: K_{j+2} is requested into K_j's tile right after the barrier that
+//    follows S_j, and published by the same barrier one step later;
 //  * V_j is requested only after tile j passed its gate; its loads overlap
 //    the softmax of the tile (one-unit kernel: into registers, then written to
 //    LDS; paired kernel: straight into LDS).  The A operand of
@@ -50,7 +51,13 @@
 //    and l sums the bf16-rounded P~ that multiplies V;
 //  * barriers fence LDS only, so outstanding global loads stay in flight; the
 //    paired kernel's barrier does not wait for direct-to-LDS loads either: a
-//    wave waits for its own before the barrier that publishes the tile;
+//    wave waits for its own before the barrier that publishes the tile.  The
+//    paired kernel takes its second barrier of a step only when some unit
+//    keeps a tile of it;
+//  * paired kernel: the softmax and P.V run in two halves of the step's keys,
+//    and after the second barrier the two units take the second half in
+//    opposite orders, so that one wave's P.V overlaps the other wave's
+//    exponentials on the same SIMD;
 //  * workgroups are ordered heaviest query block first (causal) and, when the
 //    grid allows, remapped so that the query heads of one KV group run back
 //    to back on the same XCD and share K_j/V_j in that XCD's L2.
@@ -532,8 +539,8 @@ __global__ void __launch_bounds__(BM * 2) bsfa_fwd_kernel(const FwdParams p) {
 // read the same K/V stream - two query heads of one KV group on the same query
 // block, or (bidirectional) two neighbouring query blocks of one head.  Two
 // waves share each SIMD; every wave keeps its 32 rows of Q in registers, and
-// K_j is loaded once for both units, straight into LDS, one step ahead into
-// the second of two K tiles.  Each unit keeps its own gate,
+// K_j is loaded once for both units, straight into LDS, two steps ahead into
+// one of two K tiles.  Each unit keeps its own gate,
 // statistics and output; V_j is requested when at least one unit keeps tile j
 // and a unit that skipped the tile neither reads it nor updates anything.
 // ---------------------------------------------------------------------------
@@ -715,10 +722,10 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
   // Direct-to-LDS load of the K or V tile of the step whose first key is row0:
   // instruction n of wave w fills the 1 KB of chunks (w DMA + n) 64 .. + 63,
   // lane l the chunk at position l of them, with the logical chunk that the
-  // swizzle puts there.  tmask: the step's key tiles to load.
+  // swizzle puts there.  tmask: the step's key tiles to load.  Buffer loads:
+  // the head's K or V is the buffer (its range is the head's own rows), the
+  // tile's first row a scalar offset, the chunk a 32-bit lane offset.
   const int ws = __builtin_amdgcn_readfirstlane(w);
-  // Buffer loads: the head's K or V as a buffer resource (scalar), the tile's
-  // first row as a scalar offset, the chunk as a 32-bit lane offset.
   auto dma_tile = [&](char* dst, const u32x4* head, int row0, bool is_k, int tmask) {
     // with tails, the lane offsets are formed here at each call rather than
     // kept across the loop (registers)
