@@ -617,7 +617,6 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
   using P2 = PairCfg<D, BM, KN>;
   constexpr int KBS = C::KB / SUB;      // 32-key sub-blocks per key tile
   constexpr int PCS = C::PC / SUB;      // 16-key P.V chunks per key tile
-  static_assert(HEADPAIR || !CAUSAL, "block pairs are for bidirectional attention");
   static_assert(C::ND == 1, "the causal diagonal fills one step");
   // K (two buffers) and V tiles in LDS: dense rows of 2D bytes with swizzled
   // 16-byte chunks, filled by direct-to-LDS loads of 1 KB per instruction
@@ -639,7 +638,7 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
   const int hh = lane >> 5;
 
   // ---- work item (a1): workgroup -> (b, KV group, two units) --------------
-  const int per_group = HEADPAIR ? p.G / 2 : p.G;  // workgroups per KV group and block (pair)
+  const int per_group = HEADPAIR ? p.pair_hn / 2 : p.pair_hn;  // workgroups per KV group and block (pair)
   int L = blockIdx.x;
   if (p.remap) {
     const int x = L & 7;
@@ -655,13 +654,14 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
   int hq_u[2], i_u[2];
   if (HEADPAIR) {
     const int i = CAUSAL ? (p.M - 1 - L) : L;  // causal: heaviest query blocks first
-    hq_u[0] = g * p.G + 2 * hin;
+    hq_u[0] = g * p.G + p.pair_h0 + 2 * hin;
     hq_u[1] = hq_u[0] + 1;
     i_u[0] = i_u[1] = i;
   } else {
-    hq_u[0] = hq_u[1] = g * p.G + hin;
-    i_u[0] = 2 * L;
-    i_u[1] = 2 * L + 1;
+    const int ip = CAUSAL ? (p.M / 2 - 1 - L) : L;  // causal: heaviest block pairs first
+    hq_u[0] = hq_u[1] = g * p.G + p.pair_h0 + hin;
+    i_u[0] = 2 * ip;
+    i_u[1] = 2 * ip + 1;
   }
   const int hq = hq_u[u];
   const int i = i_u[u];
@@ -698,15 +698,16 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
   for (int uu = 0; uu < 2; ++uu)
     tau_u[uu] = MAXONLY ? INFINITY : p.thresholds[hq_u[uu] * p.T_len + min(i_u[uu], p.T_len - 1)];
   const float c2 = p.scale_log2;
-  // diagonal key blocks of each unit; under causal masking both units have the
-  // same query block, so the last visited key block is the same for both
+  // diagonal key blocks of each unit.  Under causal masking a head pair shares
+  // its query block; in a block pair the second unit's diagonal comes later,
+  // and tiles past the first unit's diagonal do not exist for it
   int jd0_u[2], jd1_u[2];
 #pragma unroll
   for (int uu = 0; uu < 2; ++uu) {
     jd0_u[uu] = diag_first<BM, BN>(i_u[uu]);
     jd1_u[uu] = diag_last<BM, BN>(i_u[uu], mkv_seq);
   }
-  const int jend = CAUSAL ? jd1_u[0] : mkv_seq - 1;  // last computed key tile
+  const int jend = CAUSAL ? jd1_u[1] : mkv_seq - 1;  // last computed key tile (of either unit)
   const int send = jend / SUB;                        // last step
   const size_t diag_row = ((size_t)(b * p.Hq + hq) * p.M + i) * p.Mkv;
 
@@ -775,7 +776,13 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
     // ---- (a4) S^T = K Q^T over the step's keys -------------------------------
     f32x16 s[C::KB];
     qk_tile_swz<D, BM, KN>(s, k_cur, l32, hh, qf);
-    if constexpr (CAUSAL && DIAG_TILE) mask_causal(s, qloc, hh, i * BM - js * KN);
+    if constexpr (CAUSAL && DIAG_TILE) {
+      mask_causal(s, qloc, hh, i * BM - js * KN);
+    } else if constexpr (CAUSAL && !HEADPAIR && decltype(KBUF)::value == 1) {
+      // causal block pair: the first unit's diagonal may fall one step before
+      // the last (the step before the last always reads buffer 1)
+      if (js == send - 1 && js >= jd0_u[0] / SUB) mask_causal(s, qloc, hh, i * BM - js * KN);
+    }
     if constexpr (RAGGED) {
       const int rows_left = n_seq - i * BM, keys_left = n_seq - js * KN;
       if (rows_left < BM || keys_left < KN) mask_tail(s, qloc, hh, rows_left, keys_left);
@@ -805,12 +812,16 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
     if (!(CAUSAL && DIAG_TILE) && js + 2 <= send) dma_tile(k_cur, kg, (js + 2) * KN, true, (1 << SUB) - 1);
     // gates in increasing key-tile order (the gap gate's running maximum)
     int skip_of[2][SUB];
+    bool ex_of[2][SUB];
 #pragma unroll
     for (int uu = 0; uu < 2; ++uu)
 #pragma unroll
       for (int t = 0; t < SUB; ++t) {
         const int j = js * SUB + t;
-        const bool exists = SUB == 1 || j < mkv_seq;  // the last step may hold a tile past the end
+        // the last step may hold a tile past the end; under causal masking a
+        // tile past the unit's diagonal is not computed for it
+        const bool exists = (SUB == 1 || j < mkv_seq) && (!CAUSAL || HEADPAIR || j <= jd1_u[uu]);
+        ex_of[uu][t] = exists;
         float tm = red[decltype(KBUF)::value][uu][0][t];
 #pragma unroll
         for (int ww = 1; ww < P2::NWU; ++ww) tm = vmax(tm, red[decltype(KBUF)::value][uu][ww][t]);
@@ -829,7 +840,7 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
       const int mine = u ? skip_of[1][t] : skip_of[0][t];
       km |= (mine ? 0 : 1) << t;
       vm |= ((skip_of[0][t] & skip_of[1][t]) ? 0 : 1) << t;
-      ns += (mine && (SUB == 1 || js * SUB + t < mkv_seq)) ? 1 : 0;
+      ns += (mine && (u ? ex_of[1][t] : ex_of[0][t])) ? 1 : 0;
     }
     const int kmask = __builtin_amdgcn_readfirstlane(km);
     const int vmask = __builtin_amdgcn_readfirstlane(vm);
@@ -926,9 +937,10 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
 
   const int utid = wu * 64 + lane;  // thread index inside the unit
   constexpr int UNT = P2::NWU * 64;
+  const int jlast = CAUSAL ? jd1_u[u] : jend;  // this unit's last computed key tile
   if (MAXONLY) {
     if ((CAUSAL || RAGGED) && live)
-      for (int jj = jend + 1 + utid; jj < p.Mkv; jj += UNT) p.tile_max[diag_row + jj] = __builtin_nanf("");
+      for (int jj = jlast + 1 + utid; jj < p.Mkv; jj += UNT) p.tile_max[diag_row + jj] = __builtin_nanf("");
     return;
   }
   // ---- (a9) epilogue -------------------------------------------------------
@@ -940,7 +952,7 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
   }
   if (p.skip_counts && utid == 0 && live) p.skip_counts[(size_t)(b * p.Hq + hq) * p.M + i] = nskip;
   if (DIAG_OUT && (CAUSAL || RAGGED) && live) {
-    for (int jj = jend + 1 + utid; jj < p.Mkv; jj += UNT) {
+    for (int jj = jlast + 1 + utid; jj < p.Mkv; jj += UNT) {
       if (p.tile_state) p.tile_state[diag_row + jj] = 0;
       if (p.tile_max) p.tile_max[diag_row + jj] = __builtin_nanf("");
     }
@@ -955,12 +967,16 @@ static int launch_one(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 
+// Query heads h0 .. h0 + hn - 1 of every KV group: in pairs of heads
+// (HEADPAIR, hn even) or in pairs of neighbouring query blocks (M even).
 template <int D, int BM, int BN, bool CAUSAL, bool DIAG_OUT, bool MAXONLY, bool HEADPAIR, bool RAGGED>
-static int launch_pair(FwdParams p, hipStream_t stream) {
-  const size_t units = (size_t)p.B * p.Hq * p.M;
-  const int per_group = HEADPAIR ? p.G / 2 : p.G;
-  p.remap = ((units / 2) % (8 * (size_t)per_group) == 0) ? 1 : 0;
-  const dim3 grid((unsigned)(units / 2));
+static int launch_pair(FwdParams p, hipStream_t stream, int h0, int hn) {
+  p.pair_h0 = h0;
+  p.pair_hn = hn;
+  const int per_group = HEADPAIR ? hn / 2 : hn;
+  const size_t grid_n = (size_t)p.B * p.Hkv * per_group * (HEADPAIR ? p.M : p.M / 2);
+  p.remap = (grid_n % (8 * (size_t)per_group) == 0) ? 1 : 0;
+  const dim3 grid((unsigned)grid_n);
   const dim3 block(BM * 4);
   hipLaunchKernelGGL((bsfa_fwd_pair_kernel<D, BM, BN, CAUSAL, DIAG_OUT, MAXONLY, HEADPAIR, RAGGED>), grid, block, 0,
                      stream, p);
@@ -968,12 +984,21 @@ static int launch_pair(FwdParams p, hipStream_t stream) {
 }
 
 // Two units per workgroup when they can share one K/V stream: query-head
-// pairs when the GQA group size is even, neighbouring query blocks of one head
-// when attention is bidirectional; otherwise one unit per workgroup.
+// pairs when the GQA group size is even; neighbouring query blocks of one head
+// when the number of query blocks is even (bidirectional attention, or the
+// last head of an odd group under causal masking, whose other heads run in
+// head pairs in a launch of their own); otherwise one unit per workgroup.
 template <int D, int BM, int BN, bool CAUSAL, bool DIAG_OUT, bool MAXONLY, bool RAGGED>
 static int launch_units_r(const FwdParams& p, hipStream_t s) {
-  if (p.G % 2 == 0) return launch_pair<D, BM, BN, CAUSAL, DIAG_OUT, MAXONLY, true, RAGGED>(p, s);
-  if (!CAUSAL && p.M % 2 == 0) return launch_pair<D, BM, BN, false, DIAG_OUT, MAXONLY, false, RAGGED>(p, s);
+  if (p.G % 2 == 0) return launch_pair<D, BM, BN, CAUSAL, DIAG_OUT, MAXONLY, true, RAGGED>(p, s, 0, p.G);
+  if (p.M % 2 == 0) {
+    if (!CAUSAL) return launch_pair<D, BM, BN, false, DIAG_OUT, MAXONLY, false, RAGGED>(p, s, 0, p.G);
+    if (p.G > 1) {
+      const int st = launch_pair<D, BM, BN, CAUSAL, DIAG_OUT, MAXONLY, true, RAGGED>(p, s, 0, p.G - 1);
+      if (st) return st;
+    }
+    return launch_pair<D, BM, BN, CAUSAL, DIAG_OUT, MAXONLY, false, RAGGED>(p, s, p.G - 1, 1);
+  }
   return launch_one<D, BM, BN, CAUSAL, DIAG_OUT, MAXONLY, RAGGED>(p, s);
 }
 

@@ -26,6 +26,8 @@ struct FwdParams {
   float scale_log2;  // scale * log2(e)
   int remap;         // 1: XCD-aware workgroup order applies (grid % (8 * G) == 0)
   int gate;          // 0: threshold gate (s_max < tau); 1: gap gate (s_max < running max - tau)
+  int pair_h0;       // paired launches: first query head, inside its KV group, that the launch covers
+  int pair_hn;       // paired launches: query heads per KV group that the launch covers
 };
 
 // Enqueue the forward kernel for B_M x B_N tiles (bm, bn in {64, 128});

@@ -33,8 +33,15 @@ CASES = {
     "headpair-causal-64x128": (dict(base="llama8k", seq_len=1024, heads_q=2, heads_kv=1), (64, 128), 3, "calib"),
     "headpair-causal-128x64-d64": (dict(base="tiny", seq_len=1024, heads_q=4, heads_kv=2), (128, 64), 5, "calib"),
     "headpair-causal-64x128-d64": (dict(base="tiny", seq_len=1024, heads_q=2, heads_kv=1), (64, 128), 2, "calib"),
-    "one-unit-causal-128x64": (dict(base="llama8k", seq_len=1024, heads_q=3, heads_kv=1), (128, 64), 4, "calib"),
-    "one-unit-causal-64x128": (dict(base="llama8k", seq_len=1024, heads_q=3, heads_kv=1), (64, 128), 2, "calib"),
+    # odd group, causal: head pairs plus causal block pairs for the last head (M even), one unit per workgroup (M odd)
+    "odd-group-causal-128x64": (dict(base="llama8k", seq_len=1024, heads_q=3, heads_kv=1), (128, 64), 4, "calib"),
+    "odd-group-causal-64x128": (dict(base="llama8k", seq_len=1024, heads_q=3, heads_kv=1), (64, 128), 2, "calib"),
+    "one-unit-causal-128x64": (dict(base="llama8k", seq_len=1152, heads_q=3, heads_kv=1), (128, 64), 4, "calib"),
+    "one-unit-causal-64x128": (dict(base="llama8k", seq_len=1088, heads_q=3, heads_kv=1), (64, 128), 2, "calib"),
+    "blockpair-causal-128x64": (dict(base="llama8k", seq_len=1024, heads_q=1, heads_kv=1), (128, 64), 5, "calib"),
+    "blockpair-causal-64x128": (dict(base="llama8k", seq_len=1024, heads_q=2, heads_kv=2), (64, 128), 3, "calib"),
+    "ragged-blockpair-causal-128x64-d64": (dict(base="tiny", seq_len=1000, heads_q=2, heads_kv=2), (128, 64), 4,
+                                           "calib"),
     "blockpair-bidirectional-128x64": (dict(base="dit32k", batch=1, heads_q=1, heads_kv=1, seq_len=1024,
                                             grid=(4, 8, 32)), (128, 64), 5, "calib"),
     "blockpair-bidirectional-64x128": (dict(base="dit32k", batch=2, heads_q=1, heads_kv=1, seq_len=1024,

@@ -5,8 +5,10 @@ lengths, each attended alone) through the C ABI:
   thresholds kept 2e-3 away from every tile maximum of every sequence);
 * every sequence bit-identical to bsfa_prefill on a copy of that sequence;
 * diagnostics past a sequence's last key block read as not computed;
-* routes: head pairs (causal), block pairs whose second block lies past the end
-  of a sequence (bidirectional), a sequence of length 0.
+* routes: head pairs (causal); block pairs whose second block lies past the end
+  of a sequence (bidirectional); an odd group under causal masking (head pairs
+  plus causal block pairs for its last head); one unit per workgroup (odd group,
+  odd number of query blocks); a sequence of length 0.
 """
 
 import numpy as np
@@ -24,7 +26,8 @@ CASES = {
     "headpair-causal": (dict(base="llama8k", batch=3, seq_len=1024, heads_q=4, heads_kv=1), [1000, 257, 640], 3),
     "blockpair-bidirectional": (dict(base="llama8k", batch=3, seq_len=1024, heads_q=3, heads_kv=1, causal=False),
                                 [900, 300, 1024], 2),
-    "one-unit-with-empty": (dict(base="tiny", batch=3, seq_len=640, heads_q=3, heads_kv=1), [0, 640, 333], 3),
+    "odd-group-with-empty": (dict(base="tiny", batch=3, seq_len=640, heads_q=3, heads_kv=1), [0, 640, 333], 3),
+    "one-unit-odd-M": (dict(base="tiny", batch=3, seq_len=576, heads_q=3, heads_kv=1), [576, 0, 300], 3),
 }
 
 
@@ -113,7 +116,7 @@ def test_varlen_writes_nothing_past_each_sequence():
     # everything of an empty sequence must keep them
     assert torch.cuda.is_available(), "GPU tests need an MI355X"
     bb.load_library()
-    over, lens, k = CASES["one-unit-with-empty"]
+    over, lens, k = CASES["odd-group-with-empty"]
     over = dict(over)
     w = wl.get_config(over.pop("base"), **over)
     data = wl.generate(w, seed=0)
