@@ -265,6 +265,22 @@ __device__ __forceinline__ void mask_causal(f32x16 (&s)[NKB], int qloc, int hh, 
     }
 }
 
+// The same mask by integer arithmetic, for code where the compare masks of
+// mask_causal would cost registers: -inf is added to the score of a hidden
+// key, 0 to a visible one (exact for finite scores).
+template <int NKB>
+__device__ __forceinline__ void mask_causal_alu(f32x16 (&s)[NKB], int qloc, int hh, int off) {
+  const int lim = qloc + off - 4 * hh;  // hidden iff kb*32 + 8(r/4) + r%4 > lim
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kc = kb * 32 + 8 * (r >> 2) + (r & 3);
+      const unsigned pen = (unsigned)((lim - kc) >> 31) & 0xFF800000u;  // -inf iff kc > lim, else +0
+      s[kb][r] += __builtin_bit_cast(float, pen);
+    }
+}
+
 // S^T = K_j Q_i^T for this wave's 32 query rows.
 // s[kb][r] = raw score of query row (lane % 32) and key kb*32 + 8(r/4) + 4(lane/32) + r%4.
 template <int D, int BM, int BN, int NKB, int NKC>
@@ -781,7 +797,7 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
     } else if constexpr (CAUSAL && !HEADPAIR && decltype(KBUF)::value == 1) {
       // causal block pair: the first unit's diagonal may fall one step before
       // the last (the step before the last always reads buffer 1)
-      if (js == send - 1 && js >= jd0_u[0] / SUB) mask_causal(s, qloc, hh, i * BM - js * KN);
+      if (js == send - 1 && js >= jd0_u[0] / SUB) mask_causal_alu(s, qloc, hh, i * BM - js * KN);
     }
     if constexpr (RAGGED) {
       const int rows_left = n_seq - i * BM, keys_left = n_seq - js * KN;
