@@ -246,8 +246,11 @@ __device__ __forceinline__ void mask_tail(f32x16 (&s)[NKB], int qloc, int hh, in
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
+      // -inf added (arithmetically, no compare masks) iff the row or the key
+      // lies past the end
       const int key = kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      if (qloc >= rows_left || key >= keys_left) s[kb][r] = -INFINITY;
+      const unsigned pen = (unsigned)(((rows_left - 1 - qloc) | (keys_left - 1 - key)) >> 31) & 0xFF800000u;
+      s[kb][r] += __builtin_bit_cast(float, pen);
     }
 }
 
