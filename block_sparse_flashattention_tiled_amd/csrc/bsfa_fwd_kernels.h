@@ -677,7 +677,7 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
     hq_u[1] = hq_u[0] + 1;
     i_u[0] = i_u[1] = i;
   } else {
-    const int ip = CAUSAL ? (p.M / 2 - 1 - L) : L;  // causal: heaviest block pairs first
+    const int ip = CAUSAL ? ((p.M + 1) / 2 - 1 - L) : L;  // causal: heaviest block pairs first
     hq_u[0] = hq_u[1] = g * p.G + p.pair_h0 + hin;
     i_u[0] = 2 * ip;
     i_u[1] = 2 * ip + 1;
@@ -987,13 +987,15 @@ static int launch_one(const FwdParams& p, hipStream_t stream) {
 }
 
 // Query heads h0 .. h0 + hn - 1 of every KV group: in pairs of heads
-// (HEADPAIR, hn even) or in pairs of neighbouring query blocks (M even).
+// (HEADPAIR, hn even) or in pairs of neighbouring query blocks (with M odd
+// the last pair's second block lies past the end: tail-handling instances
+// only).
 template <int D, int BM, int BN, bool CAUSAL, bool DIAG_OUT, bool MAXONLY, bool HEADPAIR, bool RAGGED>
 static int launch_pair(FwdParams p, hipStream_t stream, int h0, int hn) {
   p.pair_h0 = h0;
   p.pair_hn = hn;
   const int per_group = HEADPAIR ? hn / 2 : hn;
-  const size_t grid_n = (size_t)p.B * p.Hkv * per_group * (HEADPAIR ? p.M : p.M / 2);
+  const size_t grid_n = (size_t)p.B * p.Hkv * per_group * (HEADPAIR ? p.M : (p.M + 1) / 2);
   p.remap = (grid_n % (8 * (size_t)per_group) == 0) ? 1 : 0;
   const dim3 grid((unsigned)grid_n);
   const dim3 block(BM * 4);
@@ -1010,15 +1012,19 @@ static int launch_pair(FwdParams p, hipStream_t stream, int h0, int hn) {
 template <int D, int BM, int BN, bool CAUSAL, bool DIAG_OUT, bool MAXONLY, bool RAGGED>
 static int launch_units_r(const FwdParams& p, hipStream_t s) {
   if (p.G % 2 == 0) return launch_pair<D, BM, BN, CAUSAL, DIAG_OUT, MAXONLY, true, RAGGED>(p, s, 0, p.G);
-  if (p.M % 2 == 0) {
-    if (!CAUSAL) return launch_pair<D, BM, BN, false, DIAG_OUT, MAXONLY, false, RAGGED>(p, s, 0, p.G);
-    if (p.G > 1) {
-      const int st = launch_pair<D, BM, BN, CAUSAL, DIAG_OUT, MAXONLY, true, RAGGED>(p, s, 0, p.G - 1);
-      if (st) return st;
-    }
-    return launch_pair<D, BM, BN, CAUSAL, DIAG_OUT, MAXONLY, false, RAGGED>(p, s, p.G - 1, 1);
+  // block pairs for heads h0 .. h0 + hn - 1; an odd number of query blocks
+  // leaves the last pair's second block past the end, which the tail-handling
+  // instances treat as a unit that writes nothing
+  auto block_pairs = [&](int h0, int hn) {
+    if (p.M % 2 == 0) return launch_pair<D, BM, BN, CAUSAL, DIAG_OUT, MAXONLY, false, RAGGED>(p, s, h0, hn);
+    return launch_pair<D, BM, BN, CAUSAL, DIAG_OUT, MAXONLY, false, true>(p, s, h0, hn);
+  };
+  if (!CAUSAL) return block_pairs(0, p.G);
+  if (p.G > 1) {
+    const int st = launch_pair<D, BM, BN, CAUSAL, DIAG_OUT, MAXONLY, true, RAGGED>(p, s, 0, p.G - 1);
+    if (st) return st;
   }
-  return launch_one<D, BM, BN, CAUSAL, DIAG_OUT, MAXONLY, RAGGED>(p, s);
+  return block_pairs(p.G - 1, 1);
 }
 
 // A sequence length that is not a multiple of both tile sides, or

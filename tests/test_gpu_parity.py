@@ -49,31 +49,32 @@ CASES = {
     "table-shorter-than-M": (dict(base="llama8k", seq_len=2048, heads_q=2, heads_kv=1), 4, "t_len4"),
     "single-tile": (dict(base="llama8k", seq_len=128, heads_q=2, heads_kv=1), None, "+inf"),
     # odd groups: causal (head pairs plus causal block pairs for the last head) and bidirectional (block pairs);
-    # bidirectional with an odd number of blocks routes to the one-unit-per-workgroup kernel
+    # an odd number of blocks leaves the last block pair's second block past the end
     "odd-group-causal": (dict(base="llama8k", seq_len=1024, heads_q=3, heads_kv=1), 3, "calib"),
     "odd-group-bidirectional-even-M": (dict(base="llama8k", seq_len=1024, heads_q=3, heads_kv=1, causal=False), 2,
                                        "calib"),
     "bidirectional-odd-M": (dict(base="dit32k", batch=1, heads_q=2, heads_kv=2, seq_len=896, grid=(4, 7, 32)), 2,
                             "calib"),
     # sequence lengths that are not a multiple of the tile (partial last block),
-    # through every route: head pairs, block pairs, one unit; both tile sizes
+    # through every route: head pairs, block pairs (even and odd M); both tile sizes
     "ragged-headpair-causal": (dict(base="llama8k", seq_len=1000, heads_q=4, heads_kv=1), 3, "calib"),
     "ragged-blockpair-bidirectional": (dict(base="llama8k", seq_len=1000, heads_q=3, heads_kv=1, causal=False), 2,
                                        "calib"),
     "ragged-odd-group-causal": (dict(base="llama8k", seq_len=700, heads_q=3, heads_kv=1), 2, "calib"),
-    "ragged-one-unit-bidirectional-d64-b64": (dict(base="tiny", seq_len=900, heads_q=2, heads_kv=2, causal=False),
+    "ragged-odd-M-bidirectional-d64-b64": (dict(base="tiny", seq_len=900, heads_q=2, heads_kv=2, causal=False),
                                               2, "calib"),
     "ragged-headpair-d64-b64": (dict(base="tiny", seq_len=1000), 4, "calib"),
     "ragged-single-partial-tile": (dict(base="llama8k", seq_len=77, heads_q=2, heads_kv=1), None, "+inf"),
     "ragged-dense-bidirectional": (dict(base="llama8k", seq_len=333, heads_q=2, heads_kv=2, causal=False), None,
                                    "calib"),
     # causal block pairs (two neighbouring query blocks of one head): multi-head attention (G = 1) and the last head
-    # of an odd group, whose other heads run in head pairs; odd M keeps the one-unit kernel
+    # of an odd group, whose other heads run in head pairs; with odd M the last pair's second block lies past the end
     "mha-causal-blockpair": (dict(base="llama8k", seq_len=1024, heads_q=2, heads_kv=2), 3, "calib"),
-    "odd-group-causal-odd-M-one-unit": (dict(base="llama8k", seq_len=1152, heads_q=3, heads_kv=1), 3, "calib"),
+    "odd-group-causal-odd-M": (dict(base="llama8k", seq_len=1152, heads_q=3, heads_kv=1), 3, "calib"),
     "ragged-blockpair-causal": (dict(base="llama8k", seq_len=1000, heads_q=1, heads_kv=1), 2, "calib"),
-    "ragged-one-unit-causal-odd-M": (dict(base="llama8k", seq_len=1100, heads_q=3, heads_kv=1), 2, "calib"),
+    "ragged-odd-group-causal-odd-M": (dict(base="llama8k", seq_len=1100, heads_q=3, heads_kv=1), 2, "calib"),
     "blockpair-causal-d64-b64": (dict(base="tiny", seq_len=640, heads_q=2, heads_kv=2), 3, "calib"),
+    "mha-causal-odd-M": (dict(base="llama8k", seq_len=1152, heads_q=2, heads_kv=2), 3, "calib"),
     "odd-group-5-causal": (dict(base="llama8k", seq_len=768, heads_q=5, heads_kv=1), 2, "calib"),
     # degenerate shapes: a single token (one partial block, only the diagonal tile), and a threshold table
     # longer than the number of query blocks (entries past the last block are never read)
@@ -168,7 +169,7 @@ def test_deterministic_and_skipped_v_never_read():
 
 
 @pytest.mark.parametrize("name", ["llama-2k-G4-d128-b128", "dit-noncausal-b128", "tiny-d64-b64-batch2",
-                                  "ragged-headpair-causal", "ragged-one-unit-bidirectional-d64-b64"])
+                                  "ragged-headpair-causal", "ragged-odd-M-bidirectional-d64-b64"])
 def test_tile_max_pass(name):
     _gpu()
     w, data, thr = _make(name)

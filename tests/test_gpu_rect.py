@@ -5,8 +5,8 @@ that bypass the gate are then the key blocks overlapping the query block's
 positions (two 64-key blocks per 128-row query block, or one 128-key block
 holding a 64-row query block).  Every case runs the diagnostic entry point
 against the oracle tile by tile and the production entry point, which must
-be bit-identical to it; the routes (head pairs, block pairs, one unit per
-workgroup), partial last blocks, both gates, bf16 output, per-sequence
+be bit-identical to it; the routes (head pairs, block pairs with even and odd
+numbers of query blocks), partial last blocks, both gates, bf16 output, per-sequence
 lengths, the tile-maximum pass and the calibration kernel are covered.
 """
 
@@ -33,11 +33,12 @@ CASES = {
     "headpair-causal-64x128": (dict(base="llama8k", seq_len=1024, heads_q=2, heads_kv=1), (64, 128), 3, "calib"),
     "headpair-causal-128x64-d64": (dict(base="tiny", seq_len=1024, heads_q=4, heads_kv=2), (128, 64), 5, "calib"),
     "headpair-causal-64x128-d64": (dict(base="tiny", seq_len=1024, heads_q=2, heads_kv=1), (64, 128), 2, "calib"),
-    # odd group, causal: head pairs plus causal block pairs for the last head (M even), one unit per workgroup (M odd)
+    # odd group, causal: head pairs plus causal block pairs for the last head (M even, and M odd: the last pair's
+    # second block past the end)
     "odd-group-causal-128x64": (dict(base="llama8k", seq_len=1024, heads_q=3, heads_kv=1), (128, 64), 4, "calib"),
     "odd-group-causal-64x128": (dict(base="llama8k", seq_len=1024, heads_q=3, heads_kv=1), (64, 128), 2, "calib"),
-    "one-unit-causal-128x64": (dict(base="llama8k", seq_len=1152, heads_q=3, heads_kv=1), (128, 64), 4, "calib"),
-    "one-unit-causal-64x128": (dict(base="llama8k", seq_len=1088, heads_q=3, heads_kv=1), (64, 128), 2, "calib"),
+    "odd-group-causal-odd-M-128x64": (dict(base="llama8k", seq_len=1152, heads_q=3, heads_kv=1), (128, 64), 4, "calib"),
+    "odd-group-causal-odd-M-64x128": (dict(base="llama8k", seq_len=1088, heads_q=3, heads_kv=1), (64, 128), 2, "calib"),
     "blockpair-causal-128x64": (dict(base="llama8k", seq_len=1024, heads_q=1, heads_kv=1), (128, 64), 5, "calib"),
     "blockpair-causal-64x128": (dict(base="llama8k", seq_len=1024, heads_q=2, heads_kv=2), (64, 128), 3, "calib"),
     "ragged-blockpair-causal-128x64-d64": (dict(base="tiny", seq_len=1000, heads_q=2, heads_kv=2), (128, 64), 4,
@@ -46,7 +47,7 @@ CASES = {
                                             grid=(4, 8, 32)), (128, 64), 5, "calib"),
     "blockpair-bidirectional-64x128": (dict(base="dit32k", batch=2, heads_q=1, heads_kv=1, seq_len=1024,
                                             grid=(4, 8, 32)), (64, 128), 3, "calib"),
-    "one-unit-bidirectional-128x64": (dict(base="dit32k", batch=1, heads_q=1, heads_kv=1, seq_len=896,
+    "odd-M-bidirectional-128x64": (dict(base="dit32k", batch=1, heads_q=1, heads_kv=1, seq_len=896,
                                            grid=(4, 7, 32)), (128, 64), 4, "calib"),
     "headpair-bidirectional-64x128-d64": (dict(base="tiny", seq_len=512, heads_q=2, heads_kv=1, causal=False),
                                           (64, 128), 1, "calib"),
@@ -60,7 +61,7 @@ CASES = {
                                        "calib"),
     "ragged-queries-only-bidirectional-128x64": (dict(base="llama8k", seq_len=960, heads_q=3, heads_kv=1,
                                                       causal=False), (128, 64), 4, "calib"),
-    "ragged-one-unit-causal-64x128": (dict(base="llama8k", seq_len=700, heads_q=3, heads_kv=1), (64, 128), 2,
+    "ragged-odd-group-causal-64x128": (dict(base="llama8k", seq_len=700, heads_q=3, heads_kv=1), (64, 128), 2,
                                       "calib"),
     "ragged-bidirectional-d64-64x128": (dict(base="tiny", seq_len=900, heads_q=2, heads_kv=2, causal=False),
                                         (64, 128), 2, "calib"),
@@ -141,7 +142,7 @@ def test_rect_skipped_v_never_read():
 
 @pytest.mark.parametrize("name", ["headpair-causal-128x64", "blockpair-bidirectional-64x128",
                                   "ragged-headpair-causal-128x64", "ragged-keys-only-causal-64x128",
-                                  "one-unit-bidirectional-128x64"])
+                                  "odd-M-bidirectional-128x64"])
 def test_rect_tile_max_pass(name):
     _gpu()
     w, tile, data, thr = _make(name)

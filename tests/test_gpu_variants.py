@@ -31,11 +31,11 @@ def _setup(over):
 
 
 GAP_CASES = {
-    # routes: head pairs (G even, causal), block pairs (bidirectional), one unit (odd G, causal), d64/b64
+    # routes: head pairs (G even, causal), block pairs (bidirectional), head pairs plus block pairs (odd G, causal), d64/b64
     "gap-headpair-causal": dict(base="llama8k", seq_len=2048, heads_q=4, heads_kv=1),
     "gap-blockpair-bidirectional": dict(base="dit32k", batch=1, heads_q=2, heads_kv=2, seq_len=1024,
                                         grid=(4, 8, 32)),
-    "gap-one-unit-odd-group": dict(base="llama8k", seq_len=1024, heads_q=3, heads_kv=1),
+    "gap-odd-group": dict(base="llama8k", seq_len=1024, heads_q=3, heads_kv=1),
     "gap-d64-b64": dict(base="tiny", seq_len=1024, heads_q=2, heads_kv=1),
 }
 
@@ -74,7 +74,7 @@ def test_infinite_gap_equals_dense_threshold():
 
 @pytest.mark.parametrize("over,k", [
     (dict(base="llama8k", seq_len=2048, heads_q=4, heads_kv=1), 5),      # head pairs
-    (dict(base="llama8k", seq_len=1024, heads_q=3, heads_kv=1), 3),      # one unit
+    (dict(base="llama8k", seq_len=1024, heads_q=3, heads_kv=1), 3),      # odd group
     (dict(base="tiny", batch=2, seq_len=512, heads_q=4, heads_kv=2), 3),  # d64, b64
 ])
 def test_bf16_output(over, k):

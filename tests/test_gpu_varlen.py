@@ -7,8 +7,8 @@ lengths, each attended alone) through the C ABI:
 * diagnostics past a sequence's last key block read as not computed;
 * routes: head pairs (causal); block pairs whose second block lies past the end
   of a sequence (bidirectional); an odd group under causal masking (head pairs
-  plus causal block pairs for its last head); one unit per workgroup (odd group,
-  odd number of query blocks); a sequence of length 0.
+  plus causal block pairs for its last head), also with an odd number of query
+  blocks; a sequence of length 0.
 """
 
 import numpy as np
@@ -27,7 +27,7 @@ CASES = {
     "blockpair-bidirectional": (dict(base="llama8k", batch=3, seq_len=1024, heads_q=3, heads_kv=1, causal=False),
                                 [900, 300, 1024], 2),
     "odd-group-with-empty": (dict(base="tiny", batch=3, seq_len=640, heads_q=3, heads_kv=1), [0, 640, 333], 3),
-    "one-unit-odd-M": (dict(base="tiny", batch=3, seq_len=576, heads_q=3, heads_kv=1), [576, 0, 300], 3),
+    "odd-group-odd-M": (dict(base="tiny", batch=3, seq_len=576, heads_q=3, heads_kv=1), [576, 0, 300], 3),
 }
 
 
