@@ -14,32 +14,26 @@
 // positions overlap the query block's: j = i for square tiles, and for
 // B_M != B_N every j with j B_N < (i+1) B_M and (j+1) B_N > i B_M.
 //
-// Two kernels share this arithmetic.  The paired kernel (further below) runs
-// two query units per workgroup on one K/V stream and is the production path
-// whenever units can be paired (an even GQA group, or bidirectional attention
-// with an even number of query blocks); the one-unit kernel serves the rest.
+// One kernel runs two query units per workgroup on one K/V stream: two query
+// heads of a KV group on one query block, or two neighbouring query blocks of
+// one head (an odd group's last head, multi-head attention, bidirectional
+// attention with an odd group); every shape is served that way.
 //
 // Mapping onto CDNA4:
-//  * one-unit kernel: one workgroup per (batch, query head, query block);
-//    B_M/32 waves, wave w owns query rows [32w, 32w+32) of the block.  It is
-//    sized to run two workgroups per CU (LDS < 80 KB, <= 256 registers per
-//    lane) so that one workgroup's MFMA phases overlap the other's softmax;
+//  * 2 B_M/32 waves per workgroup, B_M/32 per unit; wave w of a unit owns its
+//    query rows [32w, 32w+32); two waves share each SIMD;
 //  * both contractions run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
 //    Scores are formed transposed, S^T = K Q^T, so that each lane ends up
 //    holding one query row: its row statistics stay in-lane and the score
 //    registers, exponentiated and rounded to bf16, are directly the B operand
 //    of O^T = V^T P^T (both operands use the same k-slot order);
-//  * Q lives in registers for the whole key loop (B.2 step (1)), in both
-//    kernels;
-//  * one-unit kernel: K_{j+1} is requested into registers before S_j is
-//    computed and written to the (row-padded) K tile in LDS once every wave is
-//    done with K_j, before V_j is requested.  Paired kernel: K goes straight
-//    from memory into LDS (buffer loads with an LDS destination), two K tiles
-//    in turn: K_{j+2} is requested into K_j's tile right after the barrier that
-//    follows S_j, and published by the same barrier one step later;
-//  * V_j is requested only after tile j passed its gate; its loads overlap
-//    the softmax of the tile (one-unit kernel: into registers, then written to
-//    LDS; paired kernel: straight into LDS).  The A operand of
+//  * Q lives in registers for the whole key loop (B.2 step (1));
+//  * K goes straight from memory into LDS (buffer loads with an LDS
+//    destination), two K tiles in turn: K_{j+2} is requested into K_j's tile
+//    right after the barrier that follows S_j, and published by the same
+//    barrier one step later;
+//  * V_j is requested only after tile j passed its gate, straight into LDS;
+//    its loads overlap the softmax of the tile.  The A operand of
 //    O^T = V^T P^T needs V transposed: it is read with ds_read_b64_tr_b16,
 //    whose 16-lane groups return a 4x16 block transposed.  The V tile is
 //    XOR-swizzled so those reads are bank-conflict free;
@@ -49,12 +43,11 @@
 //  * the running output is rescaled lazily: only when a row maximum grows by
 //    more than 2^4 (exact: O and l always refer to the same reference max),
 //    and l sums the bf16-rounded P~ that multiplies V;
-//  * barriers fence LDS only, so outstanding global loads stay in flight; the
-//    paired kernel's barrier does not wait for direct-to-LDS loads either: a
-//    wave waits for its own before the barrier that publishes the tile.  The
-//    paired kernel takes its second barrier of a step only when some unit
-//    keeps a tile of it;
-//  * paired kernel: the softmax and P.V run in two halves of the step's keys,
+//  * barriers wait for LDS instructions only, so direct-to-LDS loads stay in
+//    flight across them: a wave waits for its own before the barrier that
+//    publishes the tile.  The second barrier of a step is taken only when some
+//    unit keeps a tile of it;
+//  * the softmax and P.V run in two halves of the step's keys,
 //    and after the second barrier the two units take the second half in
 //    opposite orders, so that one wave's P.V overlaps the other wave's
 //    exponentials on the same SIMD;
@@ -83,22 +76,14 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 template <int D, int BM, int BN>
 struct Cfg {
-  static constexpr int NW = BM / 32;         // waves per workgroup (one query unit)
-  static constexpr int NT = NW * 64;         // threads per workgroup
   static constexpr int KC = D / 16;          // 16-wide d chunks of the QK^T contraction
   static constexpr int KB = BN / 32;         // 32-key sub-blocks of a tile
   static constexpr int PC = BN / 16;         // 16-key chunks of the P.V contraction
   static constexpr int DB = D / 32;          // 32-wide d sub-blocks of the output
   static constexpr int CPR = D / 8;          // 16-byte chunks per K / V row
-  static constexpr int TILE_CHUNKS = BN * CPR;  // 16-byte chunks per K or V tile
-  static constexpr int LD = TILE_CHUNKS / NT;   // 16-byte chunks per thread per K / V tile
-  static constexpr int KS = D * 2 + 16;      // K row stride in LDS (bytes): b128 reads conflict free
-  static constexpr int K_BYTES = BN * KS;
-  static constexpr int V_BYTES = BN * D * 2;  // dense, XOR-swizzled
   // diagonal tiles of a query block when both sides divide N: B_M / B_N for
   // tall tiles, else one (a query block lies inside one key block)
   static constexpr int ND = BM > BN ? BM / BN : 1;
-  static_assert(LD * NT == TILE_CHUNKS, "tile loads split evenly over the workgroup");
 };
 
 // Diagonal key blocks of query block i: [first, last], the key blocks whose
@@ -170,14 +155,6 @@ __device__ __forceinline__ float wave_max_sym(float x) {
   return vmax(e, o);
 }
 
-// Workgroup barrier that orders LDS accesses only: global loads issued before
-// it stay in flight.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // Gate of one query unit for tile j (a5).  Threshold gate (the pages'
 // method, "Block Sparse Flash Attention" Sec. 4.1 and 4.4): an off-diagonal
 // tile is skipped iff s_max < tau, strictly.  Gap gate (the comparison
@@ -230,16 +207,10 @@ __device__ __forceinline__ void store_out_row(const FwdParams& p, size_t row, co
 
 // Sequences whose length N is not a multiple of the tile: the last query and
 // key blocks are partial, and positions >= N do not exist (masked, not padded).
-// tile_chunk: index of 16-byte chunk c of the tile whose first row is r0, with
-// rows past the end reading the last row instead, so that every load stays
-// inside the tensor; mask_tail sets the scores of query rows >= rows_left and of
-// keys >= keys_left (both relative to the tile) to -inf, so the values read
-// there never reach a maximum, a sum or an output.
-template <int CPR>
-__device__ __forceinline__ size_t tile_chunk(int r0, int c, int n) {
-  const int row = min(r0 + c / CPR, n - 1);
-  return (size_t)row * CPR + c % CPR;
-}
+// Loads of rows past the end read the last row instead, so that every load
+// stays inside the tensor; mask_tail sets the scores of query rows >=
+// rows_left and of keys >= keys_left (both relative to the tile) to -inf, so
+// the values read there never reach a maximum, a sum or an output.
 template <int NKB>
 __device__ __forceinline__ void mask_tail(f32x16 (&s)[NKB], int qloc, int hh, int rows_left, int keys_left) {
 #pragma unroll
@@ -284,280 +255,11 @@ __device__ __forceinline__ void mask_causal_alu(f32x16 (&s)[NKB], int qloc, int 
     }
 }
 
-// S^T = K_j Q_i^T for this wave's 32 query rows.
-// s[kb][r] = raw score of query row (lane % 32) and key kb*32 + 8(r/4) + 4(lane/32) + r%4.
-template <int D, int BM, int BN, int NKB, int NKC>
-__device__ __forceinline__ void qk_tile(f32x16 (&s)[NKB], const char* ks, int k_lane, const bf16x8 (&qf)[NKC]) {
-  using C = Cfg<D, BM, BN>;
-  static_assert(NKB == C::KB && NKC == C::KC, "fragment sizes");
-#pragma unroll
-  for (int kb = 0; kb < C::KB; ++kb) s[kb] = f32x16{};
-  // d-chunk outer, key block inner: consecutive MFMAs use independent
-  // accumulators and the next chunk's K fragments load while they run
-#pragma unroll
-  for (int c = 0; c < C::KC; ++c) {
-    bf16x8 a[C::KB];
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-      a[kb] = *reinterpret_cast<const bf16x8*>(ks + k_lane + kb * 32 * C::KS + c * 32);
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], qf[c], s[kb], 0, 0, 0);
-  }
-}
-
-// MAXONLY: calibration pass - only the tile maxima of every computed tile are
-// produced (no gate, no V, no output); used to build threshold tables.
-template <int D, int BM, int BN, bool CAUSAL, bool DIAG_OUT, bool MAXONLY, bool RAGGED>
-__global__ void __launch_bounds__(BM * 2) bsfa_fwd_kernel(const FwdParams p) {
-  using C = Cfg<D, BM, BN>;
-  __shared__ __attribute__((aligned(16))) char v_lds[C::V_BYTES];
-  __shared__ __attribute__((aligned(16))) char k_lds[C::K_BYTES];
-  __shared__ float red[C::NW];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;
-
-  // ---- work item (a1): workgroup -> (b, query head, query block) ----------
-  int L = blockIdx.x;
-  if (p.remap) {
-    // consecutive workgroups go to consecutive XCDs; regroup so that one XCD
-    // runs the G query heads of a KV group on the same query block together
-    const int x = L & 7;
-    const int pp = L >> 3;
-    L = ((pp / p.G) * 8 + x) * p.G + (pp % p.G);
-  }
-  const int hin = L % p.G;
-  L /= p.G;
-  const int g = L % p.Hkv;
-  L /= p.Hkv;
-  const int b = L % p.B;
-  L /= p.B;
-  const int i = CAUSAL ? (p.M - 1 - L) : L;  // causal: heaviest query blocks first
-  const int hq = g * p.G + hin;
-  // length of this batch element's sequence (per-sequence lengths: clamped to
-  // [0, N]); a query block past its end has nothing to compute or write
-  const int n_seq = (RAGGED && p.seq_lens) ? min(max(p.seq_lens[b], 0), p.N) : p.N;
-  const int m_seq = RAGGED ? (n_seq + BM - 1) / BM : p.M;      // query blocks
-  const int mkv_seq = RAGGED ? (n_seq + BN - 1) / BN : p.Mkv;  // key blocks
-  if (RAGGED && i >= m_seq) return;
-
-  const size_t q_head = (size_t)(b * p.Hq + hq) * p.N;
-  const size_t kv_head = (size_t)(b * p.Hkv + g) * p.N;
-  const int qloc = 32 * w + l32;  // this lane's query row inside the block
-  const int qrow = i * BM + qloc;
-  constexpr int TILE_CHUNKS = C::TILE_CHUNKS;
-
-  // per-lane LDS byte offset of the K operand reads
-  const int k_lane = l32 * C::KS + hh * 16;
-  // ds_read_b64_tr_b16: source lane 4e + c of each 16-lane group points at
-  // V[key0 + e][d0 + 4c]; lane j of the group then receives V[key0..key0+3][d0 + j]
-  const int v_e = (lane & 15) >> 2;
-  const int v_row = 4 * hh + v_e;                       // + 16 kc + 8 half
-  const int v_col = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // 16-byte chunk, + 4 db
-  const int v_half = (lane & 1) * 8;
-  const u32x4* vg = reinterpret_cast<const u32x4*>(p.v) + kv_head * C::CPR;
-
-  // ---- (a2) Q_i stays in registers: B operand of S^T = K Q^T --------------
-  bf16x8 qf[C::KC];
-  {
-    const u32x4* qg = reinterpret_cast<const u32x4*>(p.q) + (q_head + (RAGGED ? min(qrow, n_seq - 1) : qrow)) * C::CPR;
-#pragma unroll
-    for (int c = 0; c < C::KC; ++c) qf[c] = __builtin_bit_cast(bf16x8, qg[2 * c + hh]);
-  }
-  const u32x4* kg = reinterpret_cast<const u32x4*>(p.k) + kv_head * C::CPR;
-
-  // threshold of (head, query block); blocks past the table reuse the last entry
-  const float tau = MAXONLY ? INFINITY : p.thresholds[hq * p.T_len + min(i, p.T_len - 1)];
-  const float c2 = p.scale_log2;
-  const int jd0 = diag_first<BM, BN>(i);
-  const int jd1 = diag_last<BM, BN>(i, mkv_seq);
-  const int jend = CAUSAL ? jd1 : mkv_seq - 1;
-  const size_t diag_row = ((size_t)(b * p.Hq + hq) * p.M + i) * p.Mkv;
-
-  f32x16 o[C::DB];
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db) o[db] = f32x16{};
-  float m_run = -INFINITY;  // reference max of O and l, in units of scale*log2(e)
-  float l_run = 0.f;        // sum of exp over this lane's half of the keys (for lse)
-  float lb_run = 0.f;       // the same sum over the bf16-rounded P~ (normalises O)
-  float mrun = -INFINITY;   // largest s_max of the kept tiles (gap gate)
-  int nskip = 0;
-
-  // K_0 -> LDS
-  u32x4 kreg[C::LD];
-  u32x4 vreg[C::LD];
-#pragma unroll
-  for (int it = 0; it < C::LD; ++it) {
-    const int c = tid + C::NT * it;
-    kreg[it] = kg[RAGGED ? tile_chunk<C::CPR>(0, c, n_seq) : c];
-  }
-#pragma unroll
-  for (int it = 0; it < C::LD; ++it) {
-    const int c = tid + C::NT * it;
-    *reinterpret_cast<u32x4*>(k_lds + (c / C::CPR) * C::KS + (c % C::CPR) * 16) = kreg[it];
-  }
-
-  for (int j = 0; j <= jend; ++j) {
-    lds_barrier();  // (a): K_j visible; every wave is done with V_{j-1}
-    // ---- (a3) request K_{j+1} into registers (skipped tiles included) -----
-    const bool more = j < jend;
-    if (more) {
-      const u32x4* src = kg + (size_t)(j + 1) * TILE_CHUNKS;
-#pragma unroll
-      for (int it = 0; it < C::LD; ++it) {
-        const int c = tid + C::NT * it;
-        kreg[it] = RAGGED ? kg[tile_chunk<C::CPR>((j + 1) * BN, c, n_seq)] : src[c];
-      }
-    }
-    // ---- (a4) S^T = K_j Q_i^T on MFMA --------------------------------------
-    f32x16 s[C::KB];
-    qk_tile<D, BM, BN>(s, k_lds, k_lane, qf);
-    const bool diag = (j >= jd0 && j <= jd1);
-    if (CAUSAL && diag) mask_causal(s, qloc, hh, i * BM - j * BN);
-    if (RAGGED) {
-      const int rows_left = n_seq - i * BM, keys_left = n_seq - j * BN;
-      if (rows_left < BM || keys_left < BN) mask_tail(s, qloc, hh, rows_left, keys_left);
-    }
-    // ---- (a5) tile maximum and gate ---------------------------------------
-    float rm0 = -INFINITY, rm1 = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        rm0 = vmax(rm0, s[kb][r]);
-        rm1 = vmax(rm1, s[kb][r + 1]);
-      }
-    float rm = vmax(rm0, rm1);
-    rm = max_halves(rm);  // full row max of query qloc
-    const float wm = wave_max_sym(rm);
-    if (lane == 0) red[w] = wm;
-    lds_barrier();  // (b): every wave is done with K_j; red complete
-    float tm = red[0];
-#pragma unroll
-    for (int ww = 1; ww < C::NW; ++ww) tm = vmax(tm, red[ww]);
-    const float tms = tm * p.scale;  // s_max in the scaled-score domain
-    int skip = MAXONLY ? 1 : gate_skip(p.gate, !diag, tms, tau, mrun);
-    skip = __builtin_amdgcn_readfirstlane(skip);
-    if (DIAG_OUT && tid == 0) {
-      if (p.tile_state) p.tile_state[diag_row + j] = diag ? 3 : (skip ? 2 : 1);
-      if (p.tile_max) p.tile_max[diag_row + j] = tms;
-    }
-    // K_{j+1} -> LDS (every wave has finished reading K_j), before V_j is
-    // requested: loads complete in issue order, so waiting for K_{j+1} after
-    // the V_j requests would also wait for V_j
-    if (more) {
-#pragma unroll
-      for (int it = 0; it < C::LD; ++it) {
-        const int c = tid + C::NT * it;
-        *reinterpret_cast<u32x4*>(k_lds + (c / C::CPR) * C::KS + (c % C::CPR) * 16) = kreg[it];
-      }
-    }
-    // ---- (a8) V_j requested only for a kept tile ---------------------------
-    if (!skip) {
-      const u32x4* src = vg + (size_t)j * TILE_CHUNKS;
-#pragma unroll
-      for (int it = 0; it < C::LD; ++it) {
-        const int c = tid + C::NT * it;
-        vreg[it] = RAGGED ? vg[tile_chunk<C::CPR>(j * BN, c, n_seq)] : src[c];
-      }
-    }
-    if (skip) {  // (a6): no V load, no exp, no statistics update
-      ++nskip;
-      continue;
-    }
-
-    // ---- (a7) online softmax while V_j is in flight --------------------------
-    // O and l refer to the reference max m_run; it is raised (and O, l
-    // rescaled) only when a row maximum exceeds it by more than 2^4, so
-    // P~ <= 16.  The output is normalised by the sum of the same bf16-rounded
-    // P~ that multiplies V, so the weights of a row normalise exactly; lse
-    // uses the fp32 sum.
-    const float m_tile = rm * c2;
-    const bool grow = m_tile > m_run + 4.f;
-    if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform: rescale O and l
-      const float m_new = grow ? m_tile : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-      lb_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
-      m_run = m_new;
-    }
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    float rs0 = 0.f, rs1 = 0.f, rb0 = 0.f, rb1 = 0.f;
-    bf16x8 pf[C::PC];
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int r = 0; r < 8; r += 2) {
-          f32x2 pr;
-          pr[0] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hf + r], c2, -m_run));
-          pr[1] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hf + r + 1], c2, -m_run));
-          const bf16x2 pb = __builtin_convertvector(pr, bf16x2);
-          rs0 += pr[0];
-          rs1 += pr[1];
-          if (r & 2) rb1 = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, rb1, false);
-          else rb0 = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, rb0, false);
-          pf[2 * kb + hf][r] = pb[0];
-          pf[2 * kb + hf][r + 1] = pb[1];
-        }
-    l_run += rs0 + rs1;
-    lb_run += rb0 + rb1;
-
-    // V_j -> LDS (swizzled rows); its loads overlapped the softmax
-#pragma unroll
-    for (int it = 0; it < C::LD; ++it) {
-      const int c = tid + C::NT * it;
-      const int row = c / C::CPR;
-      *reinterpret_cast<u32x4*>(v_lds + row * (2 * D) + ((c % C::CPR) ^ v_swz<D>(row)) * 16) = vreg[it];
-    }
-    lds_barrier();  // (c): V_j complete
-    // ---- (a8) O^T += V_j^T P~^T on MFMA -----------------------------------
-#pragma unroll
-    for (int kc = 0; kc < C::PC; ++kc)
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        const int row = 16 * kc + v_row;
-        const int chunk = (4 * db + v_col) ^ v_swz<D>(row);
-        const char* base = v_lds + row * (2 * D) + chunk * 16 + v_half;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * 2 * D));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kc], o[db], 0, 0, 0);
-      }
-  }
-
-  if (MAXONLY) {
-    if (CAUSAL || RAGGED)
-      for (int jj = jend + 1 + tid; jj < p.Mkv; jj += C::NT) p.tile_max[diag_row + jj] = __builtin_nanf("");
-    return;
-  }
-  // ---- (a9) epilogue: O_i = O_acc / l, lse, skip count -------------------
-  const float l_tot = sum_halves(l_run);
-  const float inv = 1.f / sum_halves(lb_run);
-  if (!RAGGED || qrow < n_seq) {
-    store_out_row(p, q_head + qrow, o, inv, hh);
-    if (p.lse && hh == 0) p.lse[q_head + qrow] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
-  }
-  if (p.skip_counts && tid == 0) p.skip_counts[(size_t)(b * p.Hq + hq) * p.M + i] = nskip;
-  if (DIAG_OUT && (CAUSAL || RAGGED)) {
-    for (int jj = jend + 1 + tid; jj < p.Mkv; jj += C::NT) {
-      if (p.tile_state) p.tile_state[diag_row + jj] = 0;
-      if (p.tile_max) p.tile_max[diag_row + jj] = __builtin_nanf("");
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
-// Paired variant: one workgroup of 2*B_M/32 waves runs two query units that
-// read the same K/V stream - two query heads of one KV group on the same query
-// block, or (bidirectional) two neighbouring query blocks of one head.  Two
-// waves share each SIMD; every wave keeps its 32 rows of Q in registers, and
+// The kernel: one workgroup of 2*B_M/32 waves runs two query units that read
+// the same K/V stream - two query heads of one KV group on the same query
+// block, or two neighbouring query blocks of one head.  Two waves share each
+// SIMD; every wave keeps its 32 rows of Q in registers, and
 // K_j is loaded once for both units, straight into LDS, two steps ahead into
 // one of two K tiles.  Each unit keeps its own gate,
 // statistics and output; V_j is requested when at least one unit keeps tile j
@@ -684,9 +386,10 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
   }
   const int hq = hq_u[u];
   const int i = i_u[u];
-  // per-sequence length (see the one-unit kernel).  A block pair whose second
-  // block lies past the end keeps that unit running through the barriers; it
-  // writes nothing
+  // Per-sequence length, clamped to [0, N]: query blocks past it exit before
+  // the first barrier.  A block pair whose second block lies past the end
+  // (per-sequence lengths, or an odd number of query blocks) keeps that unit
+  // running through the barriers; it writes nothing
   const int n_seq = (RAGGED && p.seq_lens) ? min(max(p.seq_lens[b], 0), p.N) : p.N;
   const int m_seq = RAGGED ? (n_seq + BM - 1) / BM : p.M;
   const int mkv_seq = RAGGED ? (n_seq + BN - 1) / BN : p.Mkv;
@@ -868,7 +571,12 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
     if (vmask) dma_tile(v_lds, vg, js * KN, false, vmask);
     bf16x8 pf[C::PC];
     // ---- (a7) online softmax over the kept key tiles, in two halves of the
-    // step's keys (lazy rescale, see the single-unit kernel) ------------------
+    // step's keys ----------------------------------------------------------
+    // O and l refer to the reference max m_run; it is raised (and O, l
+    // rescaled) only when a row maximum exceeds it by more than 2^4, so
+    // P~ <= 16.  The output is normalised by the sum of the same bf16-rounded
+    // P~ that multiplies V, so the weights of a row normalise exactly; lse
+    // uses the fp32 sum.
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     float rs0 = 0.f, rs1 = 0.f, rb0 = 0.f, rb1 = 0.f;
     auto softmax_half = [&](int h) {
@@ -978,14 +686,6 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
   }
 }
 
-template <int D, int BM, int BN, bool CAUSAL, bool DIAG_OUT, bool MAXONLY, bool RAGGED>
-static int launch_one(const FwdParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)((size_t)p.B * p.Hq * p.M));
-  const dim3 block(BM * 2);
-  hipLaunchKernelGGL((bsfa_fwd_kernel<D, BM, BN, CAUSAL, DIAG_OUT, MAXONLY, RAGGED>), grid, block, 0, stream, p);
-  return hipGetLastError() == hipSuccess ? 0 : 5;
-}
-
 // Query heads h0 .. h0 + hn - 1 of every KV group: in pairs of heads
 // (HEADPAIR, hn even) or in pairs of neighbouring query blocks (with M odd
 // the last pair's second block lies past the end: tail-handling instances
@@ -1004,11 +704,10 @@ static int launch_pair(FwdParams p, hipStream_t stream, int h0, int hn) {
   return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 
-// Two units per workgroup when they can share one K/V stream: query-head
-// pairs when the GQA group size is even; neighbouring query blocks of one head
-// when the number of query blocks is even (bidirectional attention, or the
-// last head of an odd group under causal masking, whose other heads run in
-// head pairs in a launch of their own); otherwise one unit per workgroup.
+// Two units per workgroup on one K/V stream: query-head pairs when the GQA
+// group size is even; otherwise neighbouring query blocks of one head (all
+// heads under bidirectional attention; under causal masking the group's last
+// head, whose other heads run in head pairs in a launch of their own).
 template <int D, int BM, int BN, bool CAUSAL, bool DIAG_OUT, bool MAXONLY, bool RAGGED>
 static int launch_units_r(const FwdParams& p, hipStream_t s) {
   if (p.G % 2 == 0) return launch_pair<D, BM, BN, CAUSAL, DIAG_OUT, MAXONLY, true, RAGGED>(p, s, 0, p.G);
