@@ -42,8 +42,6 @@ bsfa::FwdParams shape_params(const bsfa_shape& shape, const bsfa_block& block) {
   p.T_len = (int)shape.thr_len;
   p.scale = (float)(1.0 / sqrt((double)shape.head_dim));
   p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)shape.head_dim));
-  const int64_t grid = (int64_t)p.B * p.Hq * p.M;
-  p.remap = (grid % (8 * (int64_t)p.G) == 0) ? 1 : 0;
   return p;
 }
 

@@ -52,8 +52,10 @@
 //    opposite orders, so that one wave's P.V overlaps the other wave's
 //    exponentials on the same SIMD;
 //  * workgroups are ordered heaviest query block first (causal) and, when the
-//    grid allows, remapped so that the query heads of one KV group run back
-//    to back on the same XCD and share K_j/V_j in that XCD's L2.
+//    grid allows, remapped for the XCDs' L2s: head pairs so that the query
+//    heads of one KV group run back to back on the same XCD; block pairs so
+//    that each XCD runs whole query heads, their block pairs back to back.
+//    Either way the workgroups resident on an XCD share K_j/V_j in its L2.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -361,10 +363,23 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
   // ---- work item (a1): workgroup -> (b, KV group, two units) --------------
   const int per_group = HEADPAIR ? p.pair_hn / 2 : p.pair_hn;  // workgroups per KV group and block (pair)
   int L = blockIdx.x;
-  if (p.remap) {
+  const int n_pairs = (p.M + 1) / 2;  // block pairs per query head
+  int lp = 0;                         // block pairs: pair index in launch order
+  if (HEADPAIR) {
+    if (p.remap) {
+      const int x = L & 7;
+      const int pp = L >> 3;
+      L = ((pp / per_group) * 8 + x) * per_group + (pp % per_group);
+    }
+  } else if (p.remap) {
+    // each XCD runs whole query heads, one after the other, their block pairs
+    // back to back: the workgroups resident on an XCD stream one head's K/V
     const int x = L & 7;
-    const int pp = L >> 3;
-    L = ((pp / per_group) * 8 + x) * per_group + (pp % per_group);
+    const int r = L >> 3;
+    lp = r % n_pairs;
+    L = (r / n_pairs) * 8 + x;
+  } else {
+    lp = L / (p.B * p.Hkv * per_group);
   }
   const int hin = L % per_group;
   L /= per_group;
@@ -379,7 +394,7 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
     hq_u[1] = hq_u[0] + 1;
     i_u[0] = i_u[1] = i;
   } else {
-    const int ip = CAUSAL ? ((p.M + 1) / 2 - 1 - L) : L;  // causal: heaviest block pairs first
+    const int ip = CAUSAL ? (n_pairs - 1 - lp) : lp;  // causal: heaviest block pairs first
     hq_u[0] = hq_u[1] = g * p.G + p.pair_h0 + hin;
     i_u[0] = 2 * ip;
     i_u[1] = 2 * ip + 1;
@@ -696,7 +711,7 @@ static int launch_pair(FwdParams p, hipStream_t stream, int h0, int hn) {
   p.pair_hn = hn;
   const int per_group = HEADPAIR ? hn / 2 : hn;
   const size_t grid_n = (size_t)p.B * p.Hkv * per_group * (HEADPAIR ? p.M : (p.M + 1) / 2);
-  p.remap = (grid_n % (8 * (size_t)per_group) == 0) ? 1 : 0;
+  p.remap = (HEADPAIR ? grid_n % (8 * (size_t)per_group) : ((size_t)p.B * p.Hkv * per_group) % 8) == 0 ? 1 : 0;
   const dim3 grid((unsigned)grid_n);
   const dim3 block(BM * 4);
   hipLaunchKernelGGL((bsfa_fwd_pair_kernel<D, BM, BN, CAUSAL, DIAG_OUT, MAXONLY, HEADPAIR, RAGGED>), grid, block, 0,

@@ -24,7 +24,7 @@ struct FwdParams {
   int Mkv;  // key blocks, ceil(N / B_N)
   float scale;       // 1 / sqrt(d)
   float scale_log2;  // scale * log2(e)
-  int remap;         // 1: XCD-aware workgroup order applies (grid % (8 * G) == 0)
+  int remap;         // 1: XCD-aware workgroup order applies (set per paired launch)
   int gate;          // 0: threshold gate (s_max < tau); 1: gap gate (s_max < running max - tau)
   int pair_h0;       // paired launches: first query head, inside its KV group, that the launch covers
   int pair_hn;       // paired launches: query heads per KV group that the launch covers
