@@ -76,6 +76,12 @@ CASES = {
     "blockpair-causal-d64-b64": (dict(base="tiny", seq_len=640, heads_q=2, heads_kv=2), 3, "calib"),
     "mha-causal-odd-M": (dict(base="llama8k", seq_len=1152, heads_q=2, heads_kv=2), 3, "calib"),
     "odd-group-5-causal": (dict(base="llama8k", seq_len=768, heads_q=5, heads_kv=1), 2, "calib"),
+    # block-pair launches over a multiple of 8 heads take the order that runs whole heads per XCD
+    "mha-8-heads-causal": (dict(base="llama8k", seq_len=768, heads_q=8, heads_kv=8), 2, "calib"),
+    "mha-8-heads-causal-odd-M": (dict(base="llama8k", seq_len=640, heads_q=8, heads_kv=8), 2, "calib"),
+    "dit-8-heads-bidirectional": (dict(base="dit32k", batch=2, heads_q=4, heads_kv=4, seq_len=512, grid=(2, 8, 32)),
+                                  2, "calib"),
+    "odd-group-causal-8-groups": (dict(base="llama8k", seq_len=512, heads_q=24, heads_kv=8), 2, "calib"),
     # degenerate shapes: a single token (one partial block, only the diagonal tile), and a threshold table
     # longer than the number of query blocks (entries past the last block are never read)
     "single-token-causal": (dict(base="llama8k", seq_len=1, heads_q=2, heads_kv=1), 3, "calib"),

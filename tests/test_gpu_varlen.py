@@ -28,6 +28,8 @@ CASES = {
                                 [900, 300, 1024], 2),
     "odd-group-with-empty": (dict(base="tiny", batch=3, seq_len=640, heads_q=3, heads_kv=1), [0, 640, 333], 3),
     "odd-group-odd-M": (dict(base="tiny", batch=3, seq_len=576, heads_q=3, heads_kv=1), [576, 0, 300], 3),
+    # 2 x 4 heads: block pairs in the order that runs whole heads per XCD
+    "mha-8-head-slots-causal": (dict(base="llama8k", batch=2, seq_len=640, heads_q=4, heads_kv=4), [640, 390], 2),
 }
 
 
