@@ -539,7 +539,17 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
       float rm = vmax(rm0, rm1);
       rm = max_halves(rm);
       rm_t[t] = rm;
-      const float wm = wave_max_sym(rm);
+      float wm;
+      if (!DIAG_OUT && !MAXONLY && p.gate == 0) {
+        // threshold gate, no tile maxima written: the gate needs only whether
+        // some row's scaled maximum is not below tau (rounding of the positive
+        // scale is monotone, so this is the decision the tile maximum gives,
+        // NaN included).  Each wave publishes its vote as +inf or -inf.
+        const bool keep = !(rm * p.scale < (u ? tau_u[1] : tau_u[0]));
+        wm = __builtin_amdgcn_ballot_w64(keep) ? INFINITY : -INFINITY;
+      } else {
+        wm = wave_max_sym(rm);
+      }
       if (lane == 0) red[decltype(KBUF)::value][u][wu][t] = wm;
     }
     wait_vmem();             // this wave's loads of K_{js+1} have landed
