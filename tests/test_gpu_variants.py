@@ -122,3 +122,57 @@ def test_calibrate_levels_equals_single_levels_and_oracle():
         fin = np.isfinite(ref)
         np.testing.assert_allclose(got[fin], ref[fin], rtol=1e-6, atol=1e-6)
     assert np.isinf(levels[3].cpu().numpy()).all() and (levels[3].cpu().numpy() < 0).all()
+
+
+TIE_CASES = {
+    # head pairs (causal), block pairs (bidirectional), 128 x 64 tiles (two gates per step)
+    "tie-headpair-causal": (dict(base="llama8k", seq_len=1024, heads_q=4, heads_kv=1), (128, 128)),
+    "tie-blockpair-bidirectional": (dict(base="llama8k", seq_len=1024, heads_q=2, heads_kv=2, causal=False),
+                                    (128, 128)),
+    "tie-headpair-causal-128x64": (dict(base="llama8k", seq_len=1024, heads_q=4, heads_kv=1), (128, 64)),
+}
+
+
+@pytest.mark.parametrize("name", list(TIE_CASES))
+def test_threshold_ties_keep_the_tile(name):
+    """The threshold gate skips an off-diagonal tile iff s_max < tau, strictly.
+    The thresholds here sit exactly on the kernel's own fp32 tile maxima (and
+    one ulp above them), which the oracle parity cases avoid on purpose: the
+    production launch and the launch that writes the tile maxima must take the
+    same decisions, and those decisions must follow the strict comparison."""
+    over, tile = TIE_CASES[name]
+    w, data, dev = _setup(over)
+    M = -(-w.seq_len // tile[0])
+    dense = bb.prefill(dev["q"], dev["k"], dev["v"], torch.full((w.heads_q, M), -np.inf, device="cuda"), w.causal,
+                       tile, diagnostics=True)
+    torch.cuda.synchronize()
+    tmax = dense["tile_max"].cpu().numpy()[0]
+    state = dense["tile_state"].cpu().numpy()[0]
+    off = state == 1  # computed off-diagonal tiles (all kept at -inf)
+    thr = np.full((w.heads_q, M), -np.inf, dtype=np.float32)
+    n_tie = 0
+    for h in range(w.heads_q):
+        for i in range(M):
+            vals = np.sort(tmax[h, i][off[h, i]])
+            if vals.size == 0:
+                continue
+            t = np.float32(vals[vals.size // 2])
+            if (h + i) % 2:
+                t = np.nextafter(t, np.float32(np.inf))  # the tile at t is now below tau: skipped
+            else:
+                n_tie += 1  # the tile at t equals tau: kept
+            thr[h, i] = t
+    assert n_tie > 0
+    t = torch.from_numpy(thr).cuda()
+    diag = bb.prefill(dev["q"], dev["k"], dev["v"], t, w.causal, tile, diagnostics=True)
+    prod = bb.prefill(dev["q"], dev["k"], dev["v"], t, w.causal, tile)
+    torch.cuda.synchronize()
+    g = {n: x.cpu().numpy() for n, x in diag.items()}
+    assert np.array_equal(g["tile_max"], dense["tile_max"].cpu().numpy(), equal_nan=True)
+    for n in ("out", "lse", "skip_counts"):
+        assert np.array_equal(prod[n].cpu().numpy(), g[n]), f"{name}: production {n} differs from diagnostics"
+    want_skip = off & (tmax < thr[:, :, None])
+    assert np.array_equal(g["skip_counts"][0], want_skip.sum(axis=2)), name
+    assert np.array_equal(g["tile_state"][0] == 2, want_skip), name
+    ties = off & (tmax == thr[:, :, None])
+    assert ties.any() and (g["tile_state"][0][ties] == 1).all(), f"{name}: a tile at tau must be kept"
