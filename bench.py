@@ -55,10 +55,10 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
-    """sha256 over the forward kernel sources (template header and the 128 x 128 instantiation)."""
+    """sha256 over the forward kernel sources (template header, parameter block and the 128 x 128 instantiation)."""
     csrc = os.path.join(ROOT, "block_sparse_flashattention_tiled_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("bsfa_fwd_kernels.h", "bsfa_fwd_128x128.hip"):
+    for f in ("bsfa_fwd_kernels.h", "bsfa_internal.h", "bsfa_fwd_128x128.hip"):
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()
 
