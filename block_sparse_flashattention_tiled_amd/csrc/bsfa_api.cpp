@@ -27,6 +27,10 @@ int check_shape(const bsfa_shape& s, int causal, const bsfa_block& blk) {
   if (s.batch * s.n_heads_q > lim / m) return BSFA_ERR_SHAPE;    // workgroups
   if (s.n_heads_q > lim / s.thr_len) return BSFA_ERR_SHAPE;      // threshold index
   if (s.batch * s.n_heads_q > lim / s.seq_len) return BSFA_ERR_SHAPE;  // (b, h) row base
+  // one head's K or V is read as a buffer of N d 2 bytes with 32-bit signed
+  // byte offsets (the tile's first row times the row pitch, plus the lane's
+  // chunk): longer heads have no kernel
+  if (s.seq_len * s.head_dim * 2 > lim) return BSFA_ERR_UNSUPPORTED;
   return BSFA_OK;
 }
 

@@ -49,7 +49,11 @@ typedef struct {
                          maximum, and their output rows are not written.  (The
                          pages instead pad to a multiple of the tile by
                          repeating the last token, App. B.3; a caller who wants
-                         that result pads before the call.) */
+                         that result pads before the call.)  One head's K or V
+                         must fit in 2^31 - 1 bytes, N * d * 2 <= INT32_MAX
+                         (N <= 8,388,607 at d = 128, N <= 16,777,215 at
+                         d = 64): longer heads return BSFA_ERR_UNSUPPORTED;
+                         N > INT32_MAX / 2 returns BSFA_ERR_SHAPE. */
   int64_t head_dim;   /* d in {64, 128} */
   int64_t thr_len;    /* T_len >= 1: thresholds per head.  Query block i uses
                          entry min(i, T_len - 1): blocks past the table reuse

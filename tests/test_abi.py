@@ -58,6 +58,15 @@ def S(B=1, Hq=4, Hkv=2, N=1024, d=128, T=8):
         (S(T=0), 1, 128, 2),
         (S(B=0), 1, 128, 2),
         (S(N=-128), 1, 128, 2),
+        # one head's K / V must fit in 2^31 - 1 bytes (32-bit buffer offsets)
+        (S(B=1, Hq=1, Hkv=1, N=8_388_607, d=128, T=1), 1, 128, 0),
+        (S(B=1, Hq=1, Hkv=1, N=8_388_608, d=128, T=1), 1, 128, 3),
+        (S(B=1, Hq=1, Hkv=1, N=8_388_609, d=128, T=1), 1, 128, 3),
+        (S(B=1, Hq=1, Hkv=1, N=16_777_215, d=64, T=1), 0, 64, 0),
+        (S(B=1, Hq=1, Hkv=1, N=16_777_216, d=64, T=1), 0, 64, 3),
+        (S(B=1, Hq=1, Hkv=1, N=16_777_217, d=64, T=1), 0, 64, 3),
+        (S(B=1, Hq=1, Hkv=1, N=100_000_000, d=128, T=1), 1, 128, 3),
+        (S(B=1, Hq=1, Hkv=1, N=2**30 + 1, d=64, T=1), 1, 64, 2),  # beyond INT32_MAX / 2
     ],
 )
 def test_validate(lib, shape, causal, blk, status):
@@ -159,3 +168,22 @@ def test_missing_library_raises_and_nothing_falls_back(monkeypatch, tmp_path):
         bb.bsfa_validate(S(), 1, bb.make_block(128))
     with pytest.raises(RuntimeError):
         bb.status_string(0)
+
+
+def test_heads_past_32bit_offsets_rejected_by_every_entry_point(lib):
+    # N d 2 > INT32_MAX: every entry point returns BSFA_ERR_UNSUPPORTED before any launch
+    import ctypes
+
+    good = 0x100000
+    blk = bb.make_block(128)
+    long_ = bb.make_shape(1, 2, 1, 8_388_608, 128, 1)
+    ks = (ctypes.c_int64 * 1)(3)
+    pks = ctypes.cast(ks, ctypes.c_void_p)
+    assert lib.bsfa_prefill(good, good, good, good, None, None, good, long_, 1, blk, None) == 3
+    assert lib.bsfa_prefill_ex(good, good, good, good, None, None, good, long_, 1, blk, good, good, None) == 3
+    assert lib.bsfa_prefill_bf16(good, good, good, good, None, None, good, long_, 1, blk, None) == 3
+    assert lib.bsfa_prefill_gated(good, good, good, good, None, None, good, long_, 1, blk, 1, None, None, None) == 3
+    assert lib.bsfa_prefill_varlen(good, good, good, good, None, None, good, long_, 1, blk, good, None, None,
+                                   None) == 3
+    assert lib.bsfa_tile_max(good, good, good, long_, 1, blk, None) == 3
+    assert lib.bsfa_calibrate(good, long_, 1, blk, pks, 1, good, None) == 3

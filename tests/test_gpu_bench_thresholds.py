@@ -1,0 +1,136 @@
+"""GPU parity on the thresholds the benchmark times.
+
+The benchmark calibrates on the GPU: tile maxima from ``bsfa_tile_max``, then
+fixed-k midpoints from ``bsfa_calibrate`` (self-calibration on the evaluation
+inputs).  A midpoint between two fp32 maxima can lie closer than 1e-3 to
+both, so some tiles fall inside the band where either decision is correct;
+where the GPU decided such a tile differently from the float64 oracle, the
+query block is compared with the oracle under the GPU's own mask.
+
+Per workload and sweep point:
+  * the production launch (``bsfa_prefill``) is bit-identical to the
+    diagnostics launch (``bsfa_prefill_ex``) on out, lse and skip_counts;
+  * over the whole tensor, the diagnostics maxima equal the calibration
+    pass's bit for bit, every computed off-diagonal tile is skipped iff its
+    fp32 maximum is below its fp32 threshold, diagonal tiles are kept,
+    uncomputed ones marked, and skip_counts count the skipped tiles;
+  * sampled query blocks of every head (the first and the last block
+    included) match the oracle: mask exact outside the band, out within
+    max-abs 1e-2 / mean-abs 1e-3, lse within 1e-3.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_flashattention_tiled_amd import accounting as acc
+from block_sparse_flashattention_tiled_amd import binding as bb
+from block_sparse_flashattention_tiled_amd import workloads as wl
+from parity_util import compare_blocks
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "llama8k": (0.5,),
+    "llama32k": (0.6, 0.8, 0.9),
+    "gqa128k": (0.95,),
+    "dit32k": (0.75,),
+}
+
+
+def _blocks(w, M, seed):
+    """Every head: its last query block, one from the second half and one anywhere
+    (random batch element); plus the very first block."""
+    rng = np.random.default_rng(seed)
+    picks = {(0, 0, 0)}
+    for h in range(w.heads_q):
+        picks.add((int(rng.integers(w.batch)), h, M - 1))
+        picks.add((int(rng.integers(w.batch)), h, int(rng.integers(M // 2, M))))
+        picks.add((int(rng.integers(w.batch)), h, int(rng.integers(M))))
+    return sorted(picks)
+
+
+def _whole_tensor_checks(w, tmax_cal, diag, thr, prod, label):
+    """Properties of the GPU results that hold at any size (on the device)."""
+    for n in ("out", "lse", "skip_counts"):
+        assert torch.equal(prod[n], diag[n]), f"{label}: production {n} differs from the diagnostics launch"
+    tm, st = diag["tile_max"], diag["tile_state"]
+    same = (tm == tmax_cal) | (torch.isnan(tm) & torch.isnan(tmax_cal))
+    assert bool(same.all()), f"{label}: diagnostics tile maxima differ from the calibration pass"
+    M, Mkv = tm.shape[2], tm.shape[3]
+    i = torch.arange(M, device=tm.device)[:, None]
+    j = torch.arange(Mkv, device=tm.device)[None, :]
+    computed = (j <= i) if w.causal else torch.ones((M, Mkv), dtype=torch.bool, device=tm.device)
+    on_diag = j == i
+    off = computed & ~on_diag
+    tau = thr[None, :, :, None]  # [1, H, M, 1]
+    expect = torch.where(off, torch.where(tm < tau, 2, 1), torch.where(on_diag, 3, 0)).to(torch.uint8)
+    bad = st != expect
+    assert not bool(bad.any()), f"{label}: {int(bad.sum())} tile states disagree with the GPU's own maxima"
+    assert bool(torch.isnan(tm[..., ~computed]).all()) and not bool(torch.isnan(tm[..., computed]).any())
+    assert torch.equal(diag["skip_counts"], (st == 2).sum(-1).to(torch.int32))
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_bench_thresholds_parity(name):
+    assert torch.cuda.is_available()
+    w = wl.get_config(name)
+    tile = (w.block, w.block)
+    print(f"[bench-thresholds {name}] generating", flush=True)
+    data = wl.generate(w, seed=0)
+    q, k, v = (bb.bits_to_device(data[n]) for n in ("q", "k", "v"))
+    M = w.n_blocks
+    tmax = bb.tile_max(q, k, w.causal, tile)
+    blocks = _blocks(w, M, seed=17)
+    inputs = (data["q"], data["k"], data["v"], w.causal)
+    computed = acc.grid_computed_tiles(w.seq_len, w.block, w.block, w.causal) * w.batch * w.heads_q
+    for tgt in CASES[name]:
+        kk = acc.grid_k_for_target(w.seq_len, w.block, w.block, tgt, w.causal)
+        label = f"{name}@{tgt} k={kk}"
+        thr = bb.calibrate(tmax, [kk], w.causal, tile, w.seq_len, w.head_dim)[0].contiguous()
+        prod = bb.prefill(q, k, v, thr, w.causal, tile)
+        diag = bb.prefill(q, k, v, thr, w.causal, tile, diagnostics=True)
+        torch.cuda.synchronize()
+        _whole_tensor_checks(w, tmax, diag, thr, prod, label)
+        frac = float(diag["skip_counts"].sum()) / computed
+        designed = acc.grid_designed_skip_fraction(w.seq_len, w.block, w.block, kk, w.causal)
+        thr_np = thr.cpu().numpy()
+        gpu = {n: t.cpu().numpy() for n, t in diag.items()}
+        print(f"[bench-thresholds {label}] oracle on {len(blocks)} query blocks", flush=True)
+        ref = oracle.run_blocks(data["q"], data["k"], data["v"], thr_np, w.causal, tile, blocks)
+        stats = compare_blocks(gpu, ref, tile, thr_np, label, inputs=inputs)
+        print(f"[bench-thresholds {label}] skip fraction {frac:.5f} (designed {designed:.5f}) {stats}", flush=True)
+        del prod, diag, gpu
+
+
+def test_thresholds_on_gpu_maxima_use_the_mask_override():
+    # Thresholds exactly on the GPU's own fp32 k-th largest off-diagonal maximum:
+    # the GPU keeps that tile (strict '<'), while the float64 maximum of the
+    # oracle lies a rounding error below or above it, so the oracle skips about
+    # half of them.  Those blocks must match the oracle under the GPU's mask.
+    w = wl.get_config("llama8k")
+    tile = (w.block, w.block)
+    data = wl.generate(w, seed=0)
+    q, k, v = (bb.bits_to_device(data[n]) for n in ("q", "k", "v"))
+    M, kk = w.n_blocks, 18
+    tmax = bb.tile_max(q, k, w.causal, tile)[0]  # [H, M, M]
+    i = torch.arange(M, device=tmax.device)[:, None]
+    j = torch.arange(M, device=tmax.device)[None, :]
+    off = torch.where(j < i, tmax, torch.full_like(tmax, float("-inf")))
+    kth = torch.topk(off, kk, dim=-1).values[..., kk - 1]
+    thr = torch.where(torch.arange(M, device=tmax.device) > kk, kth, torch.full_like(kth, float("-inf")))
+    thr = thr.contiguous()
+    diag = bb.prefill(q, k, v, thr, w.causal, tile, diagnostics=True)
+    torch.cuda.synchronize()
+    kept_off = ((diag["tile_state"] == 1).sum(-1))[0]
+    rows = torch.arange(M, device=thr.device) > kk
+    assert bool((kept_off[:, rows] >= kk).all()), "the tile on its threshold must be kept"
+    rng = np.random.default_rng(5)
+    blocks = sorted({(0, h, int(x)) for h in range(w.heads_q) for x in rng.integers(kk + 1, M, size=2)})
+    thr_np = thr.cpu().numpy()
+    gpu = {n: t.cpu().numpy() for n, t in diag.items()}
+    ref = oracle.run_blocks(data["q"], data["k"], data["v"], thr_np, w.causal, tile, blocks)
+    stats = compare_blocks(gpu, ref, tile, thr_np, "on-maxima", inputs=(data["q"], data["k"], data["v"], True))
+    print(f"[bench-thresholds on-maxima llama8k k={kk}] {stats}", flush=True)
+    assert stats["flipped"] > 0 and stats["overridden"] > 0, "the case should exercise the mask override"

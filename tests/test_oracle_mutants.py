@@ -92,7 +92,42 @@ def _mut_calib_square(tile_max_row, i, k, causal, block=1):  # off-diagonal set 
     return 0.5 * (vals[k - 1] + vals[k])
 
 
+_ORIG_TO_F64 = ob.to_f64
+
+
+def _mut_to_f64_fp16(x):  # bf16 bits read as IEEE half precision
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return x.view(np.float16).astype(np.float64)
+    return _ORIG_TO_F64(x)
+
+
+def _mut_to_f64_shift(x):  # mantissa bits placed one position too low
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64)
+    return _ORIG_TO_F64(x)
+
+
+def _mut_override_transposed(q, k, v, thresholds, causal, block, blocks, skip_override=None,
+                             gate_mode="threshold"):  # the mask read as [.., key block, query block]
+    if skip_override is not None:
+        skip_override = np.swapaxes(skip_override, -1, -2)
+    return _ORIG_RUN_BLOCKS(q, k, v, thresholds, causal, block, blocks, skip_override, gate_mode)
+
+
+def _mut_override_ignored(q, k, v, thresholds, causal, block, blocks, skip_override=None,
+                          gate_mode="threshold"):  # the gate's own decisions kept
+    return _ORIG_RUN_BLOCKS(q, k, v, thresholds, causal, block, blocks, None, gate_mode)
+
+
 MUTANTS = [
+    ("to_f64", _mut_to_f64_fp16, pins.test_bf16_decode_matches_library_conversion),
+    ("to_f64", _mut_to_f64_shift, pins.test_bf16_decode_matches_library_conversion),
+    ("run_blocks", _mut_override_transposed,
+     lambda: pins.test_mask_override_equals_library_attention_under_the_mask(False, 256, 64)),
+    ("run_blocks", _mut_override_ignored,
+     lambda: pins.test_mask_override_equals_library_attention_under_the_mask(True, 256, 64)),
     ("gate", _mut_gate_le, lambda: pins.test_uniform_scores_tie_rule_closed_form(True)),
     ("gate", _mut_gate_no_bypass, lambda: pins.test_infinite_threshold_is_block_diagonal_attention(True)),
     ("block_scores", _mut_unscaled, lambda: pins.test_dense_threshold_equals_library_attention(True)),
@@ -113,6 +148,9 @@ MUTANTS = [
 
 @pytest.mark.parametrize("name,mutant,pin", MUTANTS, ids=[m[1].__name__ for m in MUTANTS])
 def test_pin_catches_mutant(monkeypatch, name, mutant, pin):
+    # the module's own calls and the package's re-export both see the mutant
     monkeypatch.setattr(ob, name, mutant)
+    if hasattr(oracle, name):
+        monkeypatch.setattr(oracle, name, mutant)
     with pytest.raises((AssertionError, ValueError)):
         pin()

@@ -78,6 +78,73 @@ def _nested(x):
     return oracle.to_f64(x).tolist()
 
 
+def test_bf16_decode_matches_library_conversion():
+    # every bf16 bit pattern decodes exactly as torch's bfloat16 -> float64
+    # conversion does (NaN patterns to NaN, signed zeros kept)
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.to_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 * 127  # exponent all ones, non-zero mantissa, either sign
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(ref[~nan]))
+    # closed forms: sign, 8 exponent bits (bias 127), 7 mantissa bits
+    assert oracle.to_f64(np.array([0x3F80, 0xC000, 0x3FC0, 0x0001, 0x7F7F, 0x7F80, 0xFF80], np.uint16)).tolist() == [
+        1.0, -2.0, 1.5, 2.0 ** -133, (2 - 2.0 ** -7) * 2.0 ** 127, math.inf, -math.inf]
+    # float inputs pass through unchanged
+    x = np.array([1.5, -2.25, np.inf, 3.0e-40], dtype=np.float32)
+    assert np.array_equal(oracle.to_f64(x), x.astype(np.float64))
+
+
+def _position_mask_sdpa(qf, kf, vf, skip, causal, bm, bn):
+    """SDPA (float64, CPU) under a boolean mask built from positions: key k takes
+    part for query q iff it is visible and tile (q // bm, k // bn) is not in
+    ``skip`` [B, H_q, M_Q, M_KV]."""
+    B, Hq, N, _ = qf.shape
+    G = Hq // kf.shape[1]
+    pos = np.arange(N)
+    allowed = ~skip[:, :, pos[:, None] // bm, pos[None, :] // bn]
+    if causal:
+        allowed &= (pos[None, :] <= pos[:, None])[None, None]
+    kt = torch.from_numpy(kf).repeat_interleave(G, dim=1)
+    vt = torch.from_numpy(vf).repeat_interleave(G, dim=1)
+    mask = torch.from_numpy(allowed)
+    out = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(qf), kt, vt, attn_mask=mask).numpy()
+    s = torch.from_numpy(qf) @ kt.transpose(-1, -2) / math.sqrt(qf.shape[-1])
+    lse = torch.logsumexp(s.masked_fill(~mask, -math.inf), -1).numpy()
+    return out, lse
+
+
+@pytest.mark.parametrize("causal,N,block", [(True, 256, 64), (False, 256, 64), (True, 200, (64, 32)),
+                                            (False, 224, (32, 64))])
+def test_mask_override_equals_library_attention_under_the_mask(causal, N, block):
+    # an externally supplied mask (the GPU's decisions on near-threshold tiles)
+    # replaces the gate: the oracle must equal SDPA under that mask
+    B, Hq, Hkv, d = 2, 4, 2, 32
+    bm, bn = oracle.tile_shape(block)
+    M, M_kv = -(-N // bm), -(-N // bn)
+    q, k, v = _inputs(11, B, Hq, Hkv, N, d)
+    rng = np.random.default_rng(12)
+    skip = rng.random((B, Hq, M, M_kv)) < 0.5
+    for i in range(M):
+        skip[:, :, i, oracle.diagonal_blocks(i, bm, bn, M_kv)] = False
+    thr = np.full((Hq, M), -np.inf)  # the gate alone would skip nothing
+    r = oracle.run(q, k, v, thr, causal, block, skip_override=skip)
+    ref, ref_lse = _position_mask_sdpa(oracle.to_f64(q), oracle.to_f64(k), oracle.to_f64(v), skip, causal, bm, bn)
+    np.testing.assert_allclose(r["out"], ref, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(r["lse"], ref_lse, atol=1e-12, rtol=0)
+    computed = r["tile_state"] != oracle.STATE_PRUNED
+    assert ((r["tile_state"] == oracle.STATE_SKIPPED) == (skip & computed)).all()
+    assert (r["skip_counts"] == (skip & computed).sum(-1)).all()
+    assert r["skip_counts"].sum() > 0
+    # a diagonal tile cannot be overridden to skipped
+    bad = skip.copy()
+    bad[0, 0, 0, 0] = True
+    with pytest.raises(ValueError):
+        oracle.run(q, k, v, thr, causal, block, skip_override=bad)
+
+
 @pytest.mark.parametrize(
     "causal,B,Hq,Hkv,N,d,t_len,seed",
     [
