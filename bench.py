@@ -29,7 +29,6 @@ Also reported, outside ``value``:
     the running maximum minus a gap) at several gaps;
   * ``tile_study``: the sweep on 128 x 64 tiles next to 128 x 128;
   * ``cold_cache``: each sweep point timed right after a 512 MB overwrite;
-  * ``clock``: the graphics clock sampled during the headline's timed steps;
   * ``cpu_baseline``: the CPU oracle (float64 numpy) on the host cores - whole
     layers for the tiny and 8K configurations, a bounded sample of query
     blocks for the 32K sweep and the DiT layer with the whole-layer time
@@ -51,7 +50,6 @@ import json
 import os
 import subprocess
 import sys
-import threading
 import time
 
 import numpy as np
@@ -104,72 +102,6 @@ def cpu_model() -> str:
     except OSError:
         pass
     return "unknown"
-
-
-class ClockSampler:
-    """Samples the GPU's graphics clock (amdsmi GPU metrics, every XCD) in a
-    background thread while ``running``; ``summary()`` gives MHz statistics or None."""
-
-    def __init__(self, enabled=True):
-        self.samples = []
-        self.error = None
-        self._stop = threading.Event()
-        self._thread = None
-        self._amdsmi = None
-        self._handle = None
-        if not enabled:
-            self.error = "disabled"
-            return
-        try:
-            import amdsmi
-
-            amdsmi.amdsmi_init()
-            handles = amdsmi.amdsmi_get_processor_handles()
-            if not handles:
-                raise RuntimeError("no GPU handle")
-            self._amdsmi, self._handle = amdsmi, handles[0]
-            self._read()
-        except Exception as e:  # noqa: BLE001
-            self.error = f"{type(e).__name__}: {e}"
-            self._amdsmi = None
-
-    def _read(self):
-        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
-        clks = m.get("current_gfxclks")
-        vals = [c for c in (clks if isinstance(clks, (list, tuple)) else []) if isinstance(c, (int, float))
-                and 0 < c < 10000]
-        if not vals:
-            c = m.get("current_gfxclk")
-            vals = [c] if isinstance(c, (int, float)) and 0 < c < 10000 else []
-        return vals
-
-    def _loop(self):
-        while not self._stop.is_set():
-            try:
-                self.samples.extend(self._read())
-            except Exception as e:  # noqa: BLE001
-                self.error = f"{type(e).__name__}: {e}"
-                return
-            self._stop.wait(0.002)
-
-    def __enter__(self):
-        if self._amdsmi is not None:
-            self._thread = threading.Thread(target=self._loop, daemon=True)
-            self._thread.start()
-        return self
-
-    def __exit__(self, *exc):
-        self._stop.set()
-        if self._thread is not None:
-            self._thread.join(timeout=2.0)
-
-    def summary(self):
-        if not self.samples:
-            return {"source": "amdsmi GPU metrics", "error": self.error or "no samples"}
-        a = np.array(self.samples, dtype=np.float64)
-        return {"source": "amdsmi GPU metrics (current_gfxclks of every XCD) during the headline's timed steps",
-                "samples": int(a.size), "mhz_mean": float(a.mean()), "mhz_min": float(a.min()),
-                "mhz_max": float(a.max()), "mhz_median": float(np.median(a))}
 
 
 # --------------------------------------------------------------------------------------------
@@ -317,7 +249,7 @@ class Layer:
             bb.bsfa_prefill_gated(self.q, self.k, self.v, out, self.lse, counts, pt["thr"], self.shape,
                                   int(w.causal), self.block, bb.GATES[pt["gate"]], None, None, self.stream)
 
-    def measure(self, points, steps, warmup, clock=None):
+    def measure(self, points, steps, warmup):
         """Time every point ``steps`` times (HIP events around each launch on the
         launching stream); fill per-point statistics.  Returns the step time."""
         torch, acc, w = self.torch, self.acc, self.w
@@ -332,8 +264,6 @@ class Layer:
         t_start = torch.cuda.Event(enable_timing=True)
         t_end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        if clock is not None:
-            clock.__enter__()
         t_start.record(self.stream)
         for s in range(steps):
             for pi, pt in enumerate(points):
@@ -342,8 +272,6 @@ class Layer:
                 ev[s][pi][1].record(self.stream)
         t_end.record(self.stream)
         torch.cuda.synchronize()
-        if clock is not None:
-            clock.__exit__(None, None, None)
         total_ms = t_start.elapsed_time(t_end)
         log(f"{w.name}: timed {steps} steps in {total_ms:.1f} ms")
         (bm, bn), d, n = self.tile, w.head_dim, w.seq_len
@@ -665,7 +593,6 @@ def main():
     ap.add_argument("--no-gate-study", action="store_true", help="skip the gap-gate comparison")
     ap.add_argument("--no-tile-study", action="store_true", help="skip the 128 x 64 tile comparison")
     ap.add_argument("--no-cold-cache", action="store_true", help="skip the cold-cache timing of the sweep")
-    ap.add_argument("--no-clock", action="store_true", help="do not sample the GPU clock")
     ap.add_argument("--profile", action="store_true",
                     help="headline sweep only (no studies, legs or CPU baseline): the profiled command")
     ap.add_argument("--traffic-probe", action="store_true",
@@ -717,8 +644,7 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b
-    clock = ClockSampler(enabled=not args.no_clock)
-    step_ms = lay.measure(points, args.steps, args.warmup, clock=clock)
+    step_ms = lay.measure(points, args.steps, args.warmup)
     speedups(points)
     step_flops = sum(pt["executed_flops"] for pt in points)
     sum_dur = sum(pt["ms_mean"] for pt in points)
@@ -773,7 +699,6 @@ def main():
             else "none current for this kernel source",
             "points": roofline_points(points, counters),
         },
-        "clock": clock.summary(),
     }
     props = torch.cuda.get_device_properties(0)
     res["device"] = {"name": props.name, "compute_units": props.multi_processor_count,
