@@ -60,6 +60,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 GAP_SWEEP = (1.0, 2.0, 3.0, 4.5, 6.0)  # gaps of the gate study, scaled-score units
 FWD_KERNEL = "bsfa_fwd_pair_kernel"
 COUNTERS_FILE = "bsfa_fwd_llama32k_counters.json"
+KERNEL_SOURCES = ("bsfa_fwd_kernels.h", "bsfa_fwd_pipe.h", "bsfa_internal.h", "bsfa_fwd_128x128.hip")
 
 
 def log(msg):
@@ -67,10 +68,10 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
-    """sha256 over the forward kernel sources (template header, parameter block and the 128 x 128 instantiation)."""
+    """sha256 over the forward kernel sources (template headers, parameter block and the 128 x 128 instantiation)."""
     csrc = os.path.join(ROOT, "block_sparse_flashattention_tiled_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("bsfa_fwd_kernels.h", "bsfa_internal.h", "bsfa_fwd_128x128.hip"):
+    for f in KERNEL_SOURCES:
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()
 

@@ -602,8 +602,11 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
     // P~ <= 16.  The output is normalised by the sum of the same bf16-rounded
     // P~ that multiplies V, so the weights of a row normalise exactly; lse
     // uses the fp32 sum.
+    // l sums the fp32 values, lb the bf16 ones over four independent chains,
+    // in the same order as bsfa_fwd_pipe_kernel (the two give identical bits)
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    float rs0 = 0.f, rs1 = 0.f, rb0 = 0.f, rb1 = 0.f;
+    float rs0 = 0.f, rs1 = 0.f;
+    float rb[4] = {0.f, 0.f, 0.f, 0.f};
     auto softmax_half = [&](int h) {
 #pragma unroll
       for (int kb = h * (C::KB / 2); kb < (h + 1) * (C::KB / 2); ++kb) {
@@ -618,8 +621,7 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
             const bf16x2 pb = __builtin_convertvector(pr, bf16x2);
             rs0 += pr[0];
             rs1 += pr[1];
-            if (r & 2) rb1 = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, rb1, false);
-            else rb0 = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, rb0, false);
+            rb[(r >> 1) & 3] = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, rb[(r >> 1) & 3], false);
             pf[2 * kb + hf][r] = pb[0];
             pf[2 * kb + hf][r + 1] = pb[1];
           }
@@ -674,7 +676,7 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
       if (!pv_first) pv_half(0);
       pv_half(1);
       l_run += rs0 + rs1;
-      lb_run += rb0 + rb1;
+      lb_run += (rb[0] + rb[1]) + (rb[2] + rb[3]);
     }
   };
   // Steps before the last in pairs (K in buffers 0, 1; a leading odd step in
@@ -711,6 +713,12 @@ __global__ void __launch_bounds__(BM * 4) __attribute__((amdgpu_waves_per_eu(2, 
   }
 }
 
+}  // namespace bsfa
+// the software-pipelined kernel for aligned 128 x 128 tiles at d = 128 (it
+// uses the helpers above)
+#include "bsfa_fwd_pipe.h"
+namespace bsfa {
+
 // Query heads h0 .. h0 + hn - 1 of every KV group: in pairs of heads
 // (HEADPAIR, hn even) or in pairs of neighbouring query blocks (with M odd
 // the last pair's second block lies past the end: tail-handling instances
@@ -724,8 +732,14 @@ static int launch_pair(FwdParams p, hipStream_t stream, int h0, int hn) {
   p.remap = (HEADPAIR ? grid_n % (8 * (size_t)per_group) : ((size_t)p.B * p.Hkv * per_group) % 8) == 0 ? 1 : 0;
   const dim3 grid((unsigned)grid_n);
   const dim3 block(BM * 4);
-  hipLaunchKernelGGL((bsfa_fwd_pair_kernel<D, BM, BN, CAUSAL, DIAG_OUT, MAXONLY, HEADPAIR, RAGGED>), grid, block, 0,
-                     stream, p);
+  if constexpr (D == 128 && BM == 128 && BN == 128 && !MAXONLY && !RAGGED && (HEADPAIR || !CAUSAL)) {
+    // aligned 128 x 128 tiles at d = 128, head pairs or bidirectional block
+    // pairs: the software-pipelined kernel (one barrier per step)
+    hipLaunchKernelGGL((bsfa_fwd_pipe_kernel<CAUSAL, DIAG_OUT, HEADPAIR>), grid, block, 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((bsfa_fwd_pair_kernel<D, BM, BN, CAUSAL, DIAG_OUT, MAXONLY, HEADPAIR, RAGGED>), grid, block, 0,
+                       stream, p);
+  }
   return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 

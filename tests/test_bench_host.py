@@ -116,7 +116,7 @@ def test_kernel_hash_follows_every_kernel_source(tmp_path, monkeypatch):
     monkeypatch.setattr(b, "ROOT", str(tmp_path))
     base = b.kernel_source_hash()
     assert base == _bench().kernel_source_hash()  # same sources, same hash
-    for name in ("bsfa_fwd_kernels.h", "bsfa_internal.h", "bsfa_fwd_128x128.hip"):
+    for name in b.KERNEL_SOURCES:
         f = csrc / name
         original = f.read_bytes()
         f.write_bytes(original + b"\n")
