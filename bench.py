@@ -59,6 +59,7 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
 GAP_SWEEP = (1.0, 2.0, 3.0, 4.5, 6.0)  # gaps of the gate study, scaled-score units
 FWD_KERNEL = "bsfa_fwd_pair_kernel"
+PIPE_KERNEL = "bsfa_fwd_pipe_kernel"
 COUNTERS_FILE = "bsfa_fwd_llama32k_counters.json"
 KERNEL_SOURCES = ("bsfa_fwd_kernels.h", "bsfa_fwd_pipe.h", "bsfa_internal.h", "bsfa_fwd_128x128.hip")
 
@@ -452,8 +453,14 @@ def _col(row, *names):
 
 
 def _forward_production(name: str) -> bool:
-    """The production forward instance: <D, BM, BN, CAUSAL, DIAG_OUT=false, MAXONLY=false, ...>."""
-    return FWD_KERNEL in name and ", false, false," in name
+    """A production forward instance (no diagnostics, not the tile-maximum pass):
+    bsfa_fwd_pipe_kernel<CAUSAL, DIAG_OUT=false, HEADPAIR> or
+    bsfa_fwd_pair_kernel<D, BM, BN, CAUSAL, DIAG_OUT=false, MAXONLY=false, ...>."""
+    for kernel, flags in ((PIPE_KERNEL, (1,)), (FWD_KERNEL, (4, 5))):
+        if kernel + "<" in name:
+            args = [a.strip() for a in name.split(kernel + "<", 1)[1].split(">", 1)[0].split(",")]
+            return all(args[f] == "false" for f in flags)
+    return False
 
 
 def _points_of(dispatches, steps, n_points):
@@ -684,7 +691,8 @@ def main():
         "points": public(points),
         "roofline": {
             "bound": "mfma",
-            "kernel": f"{FWD_KERNEL} (production instance: {w.block} x {w.block} tiles, d = {w.head_dim}, "
+            "kernel": f"{PIPE_KERNEL if w.block == 128 and w.head_dim == 128 else FWD_KERNEL} (production instance: "
+                      f"{w.block} x {w.block} tiles, d = {w.head_dim}, "
                       f"{'causal' if w.causal else 'bidirectional'}, "
                       f"{'head pairs' if w.group % 2 == 0 else 'block pairs'})",
             "achieved": achieved,
