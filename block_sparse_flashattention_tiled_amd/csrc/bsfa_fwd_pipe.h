@@ -34,12 +34,13 @@
 
 namespace bsfa {
 
-template <bool CAUSAL, bool DIAG_OUT, bool HEADPAIR>
+template <bool CAUSAL, bool DIAG_OUT, bool HEADPAIR, bool RAGGED>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
     bsfa_fwd_pipe_kernel(const FwdParams p) {
-  // causal block pairs (the two units' diagonals one step apart) run in
-  // bsfa_fwd_pair_kernel
+  // causal block pairs (the two units' diagonals one step apart), and block
+  // pairs with tails, run in bsfa_fwd_pair_kernel
   static_assert(!CAUSAL || HEADPAIR, "causal block pairs are not served here");
+  static_assert(!RAGGED || HEADPAIR, "block pairs with tails are not served here");
   constexpr int D = 128, BM = 128, BN = 128;
   using C = Cfg<D, BM, BN>;
   using P2 = PairCfg<D, BM, BN>;
@@ -100,6 +101,13 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
   const int hq = hq_u[u];
   const int i = i_u[u];
+  // Tails (RAGGED: a length that is not a multiple of 128, or per-sequence
+  // lengths clamped to [0, N]): the last query and key blocks are partial and
+  // positions past the end do not exist.  A query block past the end writes
+  // nothing (both units of a head pair share it).
+  const int n_seq = (RAGGED && p.seq_lens) ? min(max(p.seq_lens[b], 0), p.N) : p.N;
+  const int mkv_seq = RAGGED ? (n_seq + BN - 1) / BN : p.Mkv;
+  if (RAGGED && i * BM >= n_seq) return;
   const size_t q_head = (size_t)(b * p.Hq + hq) * p.N;
   const size_t kv_head = (size_t)(b * p.Hkv + g) * p.N;
   const int qloc = 32 * wu + l32;
@@ -115,9 +123,11 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   asm volatile("" : "+v"(vb));
 
   // ---- (a2) Q: this wave's 32 rows stay in registers as MFMA B fragments ------
+  // (a row past the end reads the last row; its scores are masked)
   bf16x8 qf[C::KC];
   {
-    const bf16x8* qsrc = reinterpret_cast<const bf16x8*>(p.q) + (q_head + qrow) * (D / 8) + hh;
+    const int qr = RAGGED ? min(qrow, n_seq - 1) : qrow;
+    const bf16x8* qsrc = reinterpret_cast<const bf16x8*>(p.q) + (q_head + qr) * (D / 8) + hh;
 #pragma unroll
     for (int c = 0; c < C::KC; ++c) qf[c] = qsrc[2 * c];
   }
@@ -129,7 +139,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int uu = 0; uu < 2; ++uu) tau_u[uu] = p.thresholds[hq_u[uu] * p.T_len + min(i_u[uu], p.T_len - 1)];
   const float c2 = p.scale_log2;
   // square tiles: the diagonal of query block i is key block i
-  const int send = CAUSAL ? i : p.Mkv - 1;  // last step (one key tile per step)
+  const int send = CAUSAL ? i : mkv_seq - 1;  // last step (one key tile per step)
   const size_t diag_row = ((size_t)(b * p.Hq + hq) * p.M + i) * p.Mkv;
 
   f32x16 o[C::DB];
@@ -163,16 +173,34 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       buffer_load_lds16(head, p.N * D * 2, dst + chunk0 * 16, voff, row0 * (C::CPR * 16) + chunk0 * 16);
     }
   };
+  // The tile that crosses the end of the sequence: lane offsets formed per
+  // lane, rows past the end reading the last row (every load stays inside
+  // the head); its scores past the end are masked.
+  auto dma_tile_tail = [&](char* dst, const u32x4* head, int row0, bool is_k) __attribute__((always_inline)) {
+    const int last = n_seq - 1 - row0;
+#pragma unroll
+    for (int n = 0; n < DMA; ++n) {
+      const int chunk0 = (w * DMA + n) * 64;
+      const int row = 4 * (w * DMA + n) + (lane >> 4);
+      const int cc = (lane & 15) ^ (is_k ? k_swz<D>(row) : v_swz<D>(row));
+      buffer_load_lds16(head, p.N * D * 2, dst + chunk0 * 16, (min(row, last) * C::CPR + cc) * 16,
+                        row0 * (C::CPR * 16));
+    }
+  };
+  auto dma_key_tile = [&](char* dst, const u32x4* head, int t, bool is_k) __attribute__((always_inline)) {
+    if (RAGGED && (t + 1) * BN > n_seq) dma_tile_tail(dst, head, t * BN, is_k);
+    else dma_tile(dst, head, t * BN, is_k);
+  };
   // Tile js (K and V alike) lives in buffer (js + par) & 1, so that the last
   // step reads buffer 0 and every buffer choice is known at compile time.
   const int par = send & 1;
-  if (par) dma_tile(k_lds1, kg, 0, true);
-  else dma_tile(k_lds0, kg, 0, true);
+  if (par) dma_key_tile(k_lds1, kg, 0, true);
+  else dma_key_tile(k_lds0, kg, 0, true);
   wait_vmem();
   lds_barrier_keep_dma();  // K_0 visible
   if (send >= 1) {         // K_1, published by the barrier of step 0
-    if (par) dma_tile(k_lds0, kg, BN, true);
-    else dma_tile(k_lds1, kg, BN, true);
+    if (par) dma_key_tile(k_lds0, kg, 1, true);
+    else dma_key_tile(k_lds1, kg, 1, true);
   }
 
   // P~V against the V tile vt: the A fragments (V^T, 32 d x 16 keys) of
@@ -211,6 +239,10 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     f32x16 s[C::KB];
     qk_tile_swz<D, BM, BN>(s, k_cur, l32, hh, qf);
     if constexpr (CAUSAL && DIAG_TILE) mask_causal(s, qloc, hh, i * BM - js * BN);
+    if constexpr (RAGGED) {
+      const int rows_left = n_seq - i * BM, keys_left = n_seq - js * BN;
+      if (rows_left < BM || keys_left < BN) mask_tail(s, qloc, hh, rows_left, keys_left);
+    }
     // ---- (a5) row maxima and this wave's vote or maximum --------------------
     float rm0 = -INFINITY, rm1 = -INFINITY;
 #pragma unroll
@@ -236,7 +268,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     wait_vmem();             // this wave's loads of K_{js+1} and V_{js-1} have landed
     lds_barrier_keep_dma();  // votes of S_js, K_{js+1} and V_{js-1} complete; K_js and V_{js-2} free
     // ---- phase B ------------------------------------------------------------
-    if (!(CAUSAL && DIAG_TILE) && js + 2 <= send) dma_tile(k_cur, kg, (js + 2) * BN, true);
+    if (!(CAUSAL && DIAG_TILE) && js + 2 <= send) dma_key_tile(k_cur, kg, js + 2, true);
     int skip_of[2];
 #pragma unroll
     for (int uu = 0; uu < 2; ++uu) {
@@ -256,7 +288,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int vmask = __builtin_amdgcn_readfirstlane((skip_of[0] & skip_of[1]) ? 0 : 1);
     nskip += mine;  // (a6)
     // ---- (a8) V_js -> LDS when some unit keeps the tile -----------------------
-    if (vmask) dma_tile(v_cur, vg, js * BN, false);
+    if (vmask) dma_key_tile(v_cur, vg, js, false);
     // ---- (a7) reference maximum of the kept tile ------------------------------
     float alpha = 1.f;
     int rescale = 0;
@@ -330,11 +362,13 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   constexpr int UNT = P2::NWU * 64;
   const float l_tot = sum_halves(l_run);
   const float inv = 1.f / sum_halves(lb_run);
-  store_out_row(p, q_head + qrow, o, inv, hh);
-  if (p.lse && hh == 0) p.lse[q_head + qrow] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
+  if (!RAGGED || qrow < n_seq) {
+    store_out_row(p, q_head + qrow, o, inv, hh);
+    if (p.lse && hh == 0) p.lse[q_head + qrow] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
+  }
   if (p.skip_counts && utid == 0) p.skip_counts[(size_t)(b * p.Hq + hq) * p.M + i] = nskip;
-  if (DIAG_OUT && CAUSAL) {
-    for (int jj = i + 1 + utid; jj < p.Mkv; jj += UNT) {
+  if (DIAG_OUT && (CAUSAL || RAGGED)) {
+    for (int jj = send + 1 + utid; jj < p.Mkv; jj += UNT) {
       if (p.tile_state) p.tile_state[diag_row + jj] = 0;
       if (p.tile_max) p.tile_max[diag_row + jj] = __builtin_nanf("");
     }

@@ -3,7 +3,9 @@
 An aligned layer with 128 x 128 tiles at d = 128 runs through the pipelined
 kernel (``bsfa_prefill``, ``bsfa_prefill_ex``); the same layer given to
 ``bsfa_prefill_varlen`` with every sequence at full length runs through the
-paired kernel's tail-handling instance.  Both form the tile maxima with the
+tail-handling instances: the paired kernel's for block pairs, the pipelined
+kernel's own for head pairs (its tail path must not change an aligned
+result either).  Both form the tile maxima with the
 same MFMA chains and reductions, gate alike, and sum the softmax and P~V in
 the same order, so out, lse, skip counts and the per-tile diagnostics must
 agree bit for bit, at any thresholds: dense, a fixed-k point calibrated on
