@@ -454,7 +454,7 @@ def _col(row, *names):
 
 def _forward_production(name: str) -> bool:
     """A production forward instance (no diagnostics, not the tile-maximum pass):
-    bsfa_fwd_pipe_kernel<CAUSAL, DIAG_OUT=false, HEADPAIR> or
+    bsfa_fwd_pipe_kernel<CAUSAL, DIAG_OUT=false, HEADPAIR, RAGGED> or
     bsfa_fwd_pair_kernel<D, BM, BN, CAUSAL, DIAG_OUT=false, MAXONLY=false, ...>."""
     for kernel, flags in ((PIPE_KERNEL, (1,)), (FWD_KERNEL, (4, 5))):
         if kernel + "<" in name:

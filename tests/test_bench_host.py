@@ -44,8 +44,8 @@ def test_counters_only_for_the_profiled_kernel_sources(tmp_path, monkeypatch):
 PROD = "void bsfa::bsfa_fwd_pair_kernel<128, 128, 128, true, false, false, true, false>(bsfa::FwdParams)"
 CALIB = "void bsfa::bsfa_fwd_pair_kernel<128, 128, 128, true, true, true, true, false>(bsfa::FwdParams)"
 DIAG = "void bsfa::bsfa_fwd_pair_kernel<128, 128, 128, true, true, false, true, false>(bsfa::FwdParams)"
-PIPE = "void bsfa::bsfa_fwd_pipe_kernel<true, false, true>(bsfa::FwdParams)"
-PIPE_DIAG = "void bsfa::bsfa_fwd_pipe_kernel<true, true, true>(bsfa::FwdParams)"
+PIPE = "void bsfa::bsfa_fwd_pipe_kernel<true, false, true, false>(bsfa::FwdParams)"
+PIPE_DIAG = "void bsfa::bsfa_fwd_pipe_kernel<true, true, true, false>(bsfa::FwdParams)"
 
 
 def test_production_instances_of_both_forward_kernels():
