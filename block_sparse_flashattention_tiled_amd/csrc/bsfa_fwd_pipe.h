@@ -37,10 +37,9 @@ namespace bsfa {
 template <bool CAUSAL, bool DIAG_OUT, bool HEADPAIR, bool RAGGED>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
     bsfa_fwd_pipe_kernel(const FwdParams p) {
-  // causal block pairs (the two units' diagonals one step apart), and block
-  // pairs with tails, run in bsfa_fwd_pair_kernel
+  // causal block pairs (the two units' diagonals one step apart) run in
+  // bsfa_fwd_pair_kernel
   static_assert(!CAUSAL || HEADPAIR, "causal block pairs are not served here");
-  static_assert(!RAGGED || HEADPAIR, "block pairs with tails are not served here");
   constexpr int D = 128, BM = 128, BN = 128;
   using C = Cfg<D, BM, BN>;
   using P2 = PairCfg<D, BM, BN>;
@@ -101,13 +100,17 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
   const int hq = hq_u[u];
   const int i = i_u[u];
-  // Tails (RAGGED: a length that is not a multiple of 128, or per-sequence
-  // lengths clamped to [0, N]): the last query and key blocks are partial and
-  // positions past the end do not exist.  A query block past the end writes
-  // nothing (both units of a head pair share it).
+  // Tails (RAGGED: a length that is not a multiple of 128, per-sequence
+  // lengths clamped to [0, N], or block pairs over an odd number of query
+  // blocks): the last query and key blocks are partial and positions past the
+  // end do not exist.  A workgroup whose units both lie past the end exits
+  // before the first barrier; a block pair whose second block lies past the end
+  // keeps that unit in the barriers (its rows masked, its decisions unused)
+  // and writes nothing for it.
   const int n_seq = (RAGGED && p.seq_lens) ? min(max(p.seq_lens[b], 0), p.N) : p.N;
   const int mkv_seq = RAGGED ? (n_seq + BN - 1) / BN : p.Mkv;
-  if (RAGGED && i * BM >= n_seq) return;
+  if (RAGGED && i_u[0] * BM >= n_seq) return;  // i_u[0] <= i_u[1]
+  const bool live = !RAGGED || i * BM < n_seq;
   const size_t q_head = (size_t)(b * p.Hq + hq) * p.N;
   const size_t kv_head = (size_t)(b * p.Hkv + g) * p.N;
   const int qloc = 32 * wu + l32;
@@ -278,7 +281,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       const float tms = tm * p.scale;
       const bool on_diag = js == i_u[uu];
       skip_of[uu] = gate_skip(p.gate, !on_diag, tms, tau_u[uu], mrun_u[uu]);
-      if (DIAG_OUT && uu == u && wu == 0 && lane == 0) {
+      if (DIAG_OUT && uu == u && wu == 0 && lane == 0 && live) {
         if (p.tile_state) p.tile_state[diag_row + js] = on_diag ? 3 : (skip_of[uu] ? 2 : 1);
         if (p.tile_max) p.tile_max[diag_row + js] = tms;
       }
@@ -366,8 +369,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     store_out_row(p, q_head + qrow, o, inv, hh);
     if (p.lse && hh == 0) p.lse[q_head + qrow] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
   }
-  if (p.skip_counts && utid == 0) p.skip_counts[(size_t)(b * p.Hq + hq) * p.M + i] = nskip;
-  if (DIAG_OUT && (CAUSAL || RAGGED)) {
+  if (p.skip_counts && utid == 0 && live) p.skip_counts[(size_t)(b * p.Hq + hq) * p.M + i] = nskip;
+  if (DIAG_OUT && (CAUSAL || RAGGED) && live) {
     for (int jj = send + 1 + utid; jj < p.Mkv; jj += UNT) {
       if (p.tile_state) p.tile_state[diag_row + jj] = 0;
       if (p.tile_max) p.tile_max[diag_row + jj] = __builtin_nanf("");
