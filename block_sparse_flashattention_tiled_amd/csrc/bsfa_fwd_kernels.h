@@ -732,10 +732,9 @@ static int launch_pair(FwdParams p, hipStream_t stream, int h0, int hn) {
   p.remap = (HEADPAIR ? grid_n % (8 * (size_t)per_group) : ((size_t)p.B * p.Hkv * per_group) % 8) == 0 ? 1 : 0;
   const dim3 grid((unsigned)grid_n);
   const dim3 block(BM * 4);
-  if constexpr (D == 128 && BM == 128 && BN == 128 && !MAXONLY && (HEADPAIR || !CAUSAL)) {
-    // 128 x 128 tiles at d = 128: head pairs and bidirectional block pairs,
-    // with or without tails, run the software-pipelined kernel (one barrier
-    // per step)
+  if constexpr (D == 128 && BM == 128 && BN == 128 && !MAXONLY) {
+    // 128 x 128 tiles at d = 128, every pairing, with or without tails: the
+    // software-pipelined kernel (one barrier per step)
     hipLaunchKernelGGL((bsfa_fwd_pipe_kernel<CAUSAL, DIAG_OUT, HEADPAIR, RAGGED>), grid, block, 0, stream, p);
   } else {
     hipLaunchKernelGGL((bsfa_fwd_pair_kernel<D, BM, BN, CAUSAL, DIAG_OUT, MAXONLY, HEADPAIR, RAGGED>), grid, block, 0,

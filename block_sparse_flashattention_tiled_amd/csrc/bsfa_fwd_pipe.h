@@ -37,9 +37,6 @@ namespace bsfa {
 template <bool CAUSAL, bool DIAG_OUT, bool HEADPAIR, bool RAGGED>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
     bsfa_fwd_pipe_kernel(const FwdParams p) {
-  // causal block pairs (the two units' diagonals one step apart) run in
-  // bsfa_fwd_pair_kernel
-  static_assert(!CAUSAL || HEADPAIR, "causal block pairs are not served here");
   constexpr int D = 128, BM = 128, BN = 128;
   using C = Cfg<D, BM, BN>;
   using P2 = PairCfg<D, BM, BN>;
@@ -142,7 +139,10 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int uu = 0; uu < 2; ++uu) tau_u[uu] = p.thresholds[hq_u[uu] * p.T_len + min(i_u[uu], p.T_len - 1)];
   const float c2 = p.scale_log2;
   // square tiles: the diagonal of query block i is key block i
-  const int send = CAUSAL ? i : mkv_seq - 1;  // last step (one key tile per step)
+  // last step (one key tile per step): the causal diagonal of a head pair,
+  // the later diagonal of a causal block pair (the second unit's, or the
+  // first's when the second lies past the end), the last key tile otherwise
+  const int send = CAUSAL ? (HEADPAIR ? i : min(i_u[1], mkv_seq - 1)) : mkv_seq - 1;
   const size_t diag_row = ((size_t)(b * p.Hq + hq) * p.M + i) * p.Mkv;
 
   f32x16 o[C::DB];
@@ -232,7 +232,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   };
 
-  auto step = [&](const int js, auto DIAGC, auto KBUF) __attribute__((always_inline)) {
+  auto step = [&](const int js, auto DIAGC, auto KBUF, auto DIAG0C) __attribute__((always_inline)) {
     constexpr bool DIAG_TILE = decltype(DIAGC)::value;
     constexpr int kb_cur = decltype(KBUF)::value;
     char* const k_cur = kb_cur ? k_lds1 : k_lds0;       // K_js
@@ -242,6 +242,11 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     f32x16 s[C::KB];
     qk_tile_swz<D, BM, BN>(s, k_cur, l32, hh, qf);
     if constexpr (CAUSAL && DIAG_TILE) mask_causal(s, qloc, hh, i * BM - js * BN);
+    if constexpr (decltype(DIAG0C)::value) {
+      // causal block pair: the first unit's diagonal, the step before the
+      // last (peeled, buffer 1); the second unit sees the whole tile
+      if (u == 0) mask_causal_alu(s, qloc, hh, i * BM - js * BN);
+    }
     if constexpr (RAGGED) {
       const int rows_left = n_seq - i * BM, keys_left = n_seq - js * BN;
       if (rows_left < BM || keys_left < BN) mask_tail(s, qloc, hh, rows_left, keys_left);
@@ -273,6 +278,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     // ---- phase B ------------------------------------------------------------
     if (!(CAUSAL && DIAG_TILE) && js + 2 <= send) dma_key_tile(k_cur, kg, js + 2, true);
     int skip_of[2];
+    bool exists_u[2];
 #pragma unroll
     for (int uu = 0; uu < 2; ++uu) {
       float tm = red[kb_cur][uu][0];
@@ -280,8 +286,10 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       for (int ww = 1; ww < P2::NWU; ++ww) tm = vmax(tm, red[kb_cur][uu][ww]);
       const float tms = tm * p.scale;
       const bool on_diag = js == i_u[uu];
-      skip_of[uu] = gate_skip(p.gate, !on_diag, tms, tau_u[uu], mrun_u[uu]);
-      if (DIAG_OUT && uu == u && wu == 0 && lane == 0 && live) {
+      // in a causal block pair the first unit has no tile past its diagonal
+      exists_u[uu] = !CAUSAL || HEADPAIR || js <= i_u[uu];
+      skip_of[uu] = exists_u[uu] ? gate_skip(p.gate, !on_diag, tms, tau_u[uu], mrun_u[uu]) : 1;
+      if (DIAG_OUT && exists_u[uu] && uu == u && wu == 0 && lane == 0 && live) {
         if (p.tile_state) p.tile_state[diag_row + js] = on_diag ? 3 : (skip_of[uu] ? 2 : 1);
         if (p.tile_max) p.tile_max[diag_row + js] = tms;
       }
@@ -289,7 +297,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int mine = u ? skip_of[1] : skip_of[0];
     const int kmask = __builtin_amdgcn_readfirstlane(mine ? 0 : 1);
     const int vmask = __builtin_amdgcn_readfirstlane((skip_of[0] & skip_of[1]) ? 0 : 1);
-    nskip += mine;  // (a6)
+    nskip += (mine && (u ? exists_u[1] : exists_u[0])) ? 1 : 0;  // (a6)
     // ---- (a8) V_js -> LDS when some unit keeps the tile -----------------------
     if (vmask) dma_key_tile(v_cur, vg, js, false);
     // ---- (a7) reference maximum of the kept tile ------------------------------
@@ -348,11 +356,18 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   };
   using KB0 = std::integral_constant<int, 0>;
   using KB1 = std::integral_constant<int, 1>;
-  for (int js = -par; js < send; js += 2) {
-    if (js >= 0) step(js, std::false_type{}, KB0{});
-    step(js + 1, std::false_type{}, KB1{});
+  // A causal block pair whose second unit is live has the first unit's
+  // diagonal one step before the last: that step is peeled as well.
+  const bool peel0 = CAUSAL && !HEADPAIR && send == i_u[0] + 1;
+  const int lend = peel0 ? send - 1 : send;  // steps [0, lend) in the loop
+  for (int js = -par; js < lend; js += 2) {
+    if (js >= 0) step(js, std::false_type{}, KB0{}, std::false_type{});
+    if (!(CAUSAL && !HEADPAIR) || js + 1 < lend) step(js + 1, std::false_type{}, KB1{}, std::false_type{});
   }
-  const int v_last = step(send, std::integral_constant<bool, CAUSAL>{}, KB0{});
+  if constexpr (CAUSAL && !HEADPAIR) {
+    if (peel0) step(send - 1, std::false_type{}, KB1{}, std::true_type{});
+  }
+  const int v_last = step(send, std::integral_constant<bool, CAUSAL>{}, KB0{}, std::false_type{});
   // ---- drain: P~V of the last step (V_send in buffer 0) --------------------------
   if (v_last) {
     wait_vmem();
@@ -371,7 +386,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
   if (p.skip_counts && utid == 0 && live) p.skip_counts[(size_t)(b * p.Hq + hq) * p.M + i] = nskip;
   if (DIAG_OUT && (CAUSAL || RAGGED) && live) {
-    for (int jj = send + 1 + utid; jj < p.Mkv; jj += UNT) {
+    const int jlast = CAUSAL ? min(i, mkv_seq - 1) : mkv_seq - 1;  // this unit's last computed key tile
+    for (int jj = jlast + 1 + utid; jj < p.Mkv; jj += UNT) {
       if (p.tile_state) p.tile_state[diag_row + jj] = 0;
       if (p.tile_max) p.tile_max[diag_row + jj] = __builtin_nanf("");
     }

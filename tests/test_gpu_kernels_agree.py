@@ -1,10 +1,10 @@
 """The forward paths return identical bits where they compute the same thing.
 
-* Pipelined kernel against the paired kernel: a causal layer whose query heads
-  share one K/V runs as head pairs (G = 2, the pipelined kernel); the same
-  query heads with that K/V repeated per head run as causal block pairs
-  (G = 1, the paired kernel).  Every (head, query block) sees the same Q rows,
-  keys, values and threshold, so out, lse, skip counts and the per-tile
+* Head pairs against causal block pairs: a causal layer whose query heads
+  share one K/V runs as head pairs (G = 2); the same query heads with that K/V
+  repeated per head run as causal block pairs (G = 1), whose two units'
+  diagonals fall one step apart.  Every (head, query block) sees the same Q
+  rows, keys, values and threshold, so out, lse, skip counts and the per-tile
   diagnostics must agree bit for bit.
 * The pipelined kernel's tail instance against its aligned one: an aligned
   layer through ``bsfa_prefill`` / ``bsfa_prefill_ex`` and through
@@ -52,7 +52,7 @@ def _assert_same(a, b, label):
     assert bool(same.all()), f"{label}: tile maxima differ"
 
 
-def test_pipelined_and_paired_kernels_agree():
+def test_head_pairs_and_causal_block_pairs_agree():
     assert torch.cuda.is_available()
     w = wl.get_config("llama8k", batch=2, seq_len=1024, heads_q=4, heads_kv=2)
     data = wl.generate(w, seed=5)
