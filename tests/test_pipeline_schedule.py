@@ -23,7 +23,7 @@ step.  After the last step, one more barrier if it requested V, then the last
 P~V.  Causal attention: the last step is the diagonal, kept by both units, and
 requests no K.  Every (last step, keep pattern) combination up to 9 steps is
 checked, for head pairs (one diagonal) and block pairs (the second unit's
-diagonal one step later, bidirectional).
+diagonal one step later, bidirectional and causal).
 """
 
 import itertools
@@ -114,6 +114,20 @@ def test_block_pair_schedule_has_no_race(send):
             keep[0][d0] = True
             keep[1][d0 + 1] = True
             check(schedule(send, keep, False))
+
+
+@pytest.mark.parametrize("send", range(1, 9))
+def test_causal_block_pair_schedule_has_no_race(send):
+    # causal block pairs: the first unit's diagonal is the step before the
+    # last (kept), the second unit's the last step (kept); the first unit has
+    # no tile in the last step
+    n = send + 1
+    for k in _patterns(n):
+        keep = [list(k), list(reversed(k))]
+        keep[0][send - 1] = True
+        keep[0][send] = False
+        keep[1][send] = True
+        check(schedule(send, keep, True))
 
 
 def test_model_detects_a_shifted_buffer_choice():
