@@ -282,6 +282,27 @@ __device__ __forceinline__ void buffer_load_lds16(const void* base, int bytes, c
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
 }
 
+// The XCD (one of the eight compute dies) the wave runs on: bits 3:0 of the
+// XCC_ID hardware register (register 20).
+__device__ __forceinline__ int xcd_id() { return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 7; }
+
+// Next work item of a persistent launch over n items.  Queue x holds the
+// items L < n with L % 8 == x in increasing order - the share of the static
+// grid that would run on XCD x, heaviest first - and work[x] counts the items
+// taken from it.  A workgroup drains its own XCD's queue, then takes from the
+// others in turn.  Returns -1 once every queue is empty; counters only grow,
+// so an empty queue stays empty.
+__device__ __forceinline__ int next_item(int* work, int n, int xcd) {
+  for (int t = 0; t < 8; ++t) {
+    const int x = (xcd + t) & 7;
+    const int nq = (n - x + 7) >> 3;
+    if (nq <= 0) continue;
+    const int idx = atomicAdd(work + x, 1);
+    if (idx < nq) return idx * 8 + x;
+  }
+  return -1;
+}
+
 // Chunk swizzle of a dense K tile in LDS (2D bytes per row): logical 16-byte
 // chunk cc of row `row` sits at position cc ^ k_swz(row), so that 16
 // consecutive rows read at one logical chunk hit distinct banks.
@@ -734,8 +755,16 @@ static int launch_pair(FwdParams p, hipStream_t stream, int h0, int hn) {
   const dim3 block(BM * 4);
   if constexpr (D == 128 && BM == 128 && BN == 128 && !MAXONLY) {
     // 128 x 128 tiles at d = 128, every pairing, with or without tails: the
-    // software-pipelined kernel (one barrier per step)
-    hipLaunchKernelGGL((bsfa_fwd_pipe_kernel<CAUSAL, DIAG_OUT, HEADPAIR, RAGGED>), grid, block, 0, stream, p);
+    // software-pipelined kernel (one barrier per step), persistent - one
+    // workgroup per compute unit taking the static grid's workgroups as work
+    // items from per-XCD queues
+    if (grid_n > (size_t)INT32_MAX) return 3;
+    int n_cu = 0;
+    p.work = pipe_work_slot(stream, &n_cu);
+    if (!p.work || n_cu <= 0) return 5;
+    p.n_items = (int)grid_n;
+    const dim3 pgrid((unsigned)(grid_n < (size_t)n_cu ? grid_n : (size_t)n_cu));
+    hipLaunchKernelGGL((bsfa_fwd_pipe_kernel<CAUSAL, DIAG_OUT, HEADPAIR, RAGGED>), pgrid, block, 0, stream, p);
   } else {
     hipLaunchKernelGGL((bsfa_fwd_pair_kernel<D, BM, BN, CAUSAL, DIAG_OUT, MAXONLY, HEADPAIR, RAGGED>), grid, block, 0,
                        stream, p);

@@ -14,9 +14,16 @@
  *
  * Conventions shared by every entry point:
  *  - Tensor pointers are DEVICE pointers owned by the caller (for instance
- *    torch tensors).  The library allocates no device memory, keeps no
- *    reference after a call returns and holds no global state; calls are
- *    reentrant.
+ *    torch tensors).  No call allocates device memory, and none keeps a
+ *    reference after it returns.
+ *  - The library's one piece of state is a ring of 1,024 slots of eight
+ *    work-queue counters per device (32 KB of module data, loaded with the
+ *    library).  Each launch of the pipelined kernel (128 x 128 tiles at
+ *    d = 128; one or two per call) takes the next slot and zeroes it on the
+ *    call's stream before the kernel, which then hands out its work items
+ *    from that slot.  Calls are therefore reentrant, on any mix of streams and
+ *    host threads, as long as at most 1,024 such launches are in flight at
+ *    once on one device.
  *  - Every argument check runs on the host before anything is enqueued; on
  *    error the call returns a non-zero status and writes nothing.
  *  - Work is enqueued on ``stream`` (a hipStream_t; NULL = the default
@@ -24,7 +31,9 @@
  *    runtime is returned as BSFA_ERR_LAUNCH; faults during execution surface
  *    at the caller's next synchronisation, as for any HIP work.
  *  - No C++ exception crosses this interface.
- *  - Results are deterministic: no atomics, fixed reduction order.
+ *  - Results are deterministic: every output element is reduced in a fixed
+ *    order whichever workgroup computes it.  The only atomics hand out work
+ *    items.
  */
 #ifndef BSFA_H
 #define BSFA_H
