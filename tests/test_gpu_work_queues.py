@@ -9,7 +9,8 @@ launch, so that an item taken twice or never shows:
 * more launches than the ring has slots, alternating a larger and a smaller
   layer on one stream, each output equal bit for bit to that layer's first;
 * launches of two layers enqueued alternately on two streams without
-  synchronisation between them, equal to the same launches run one by one.
+  synchronisation between them, equal to the same launches run one by one;
+* a launch captured in a graph and replayed, equal to the eager launch.
 """
 
 import pytest
@@ -98,3 +99,33 @@ def test_streams_overlap(causal):
     torch.cuda.synchronize()
     _same(a, ref_a, "stream 1")
     _same(b, ref_b, "stream 2")
+
+
+def test_graph_replays():
+    # a captured forward (the counter-zeroing kernel and the persistent kernel,
+    # no memset node) replayed several times, with eager work and
+    # synchronisation between the replays, each replay equal to the eager run
+    assert torch.cuda.is_available()
+    L = _layer(2048, 4, 2, True, seed=31)
+    _launch(L)
+    torch.cuda.synchronize()
+    ref = _snap(L)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            bb.bsfa_prefill(L["q"], L["k"], L["v"], L["out"], L["lse"], L["cnt"], L["thr"], L["shape"],
+                            int(L["w"].causal), L["block"], side)
+    torch.cuda.synchronize()
+    for r in range(4):
+        L["out"].fill_(float("nan"))
+        L["lse"].fill_(float("nan"))
+        L["cnt"].fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _same(L, ref, f"replay {r}")
+        _launch(L)  # eager work between the replays
+        torch.cuda.synchronize()
+        _same(L, ref, f"eager run after replay {r}")
