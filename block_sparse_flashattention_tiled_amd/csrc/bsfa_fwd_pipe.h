@@ -128,10 +128,10 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     // Tails (RAGGED: a length that is not a multiple of 128, per-sequence
     // lengths clamped to [0, N], or block pairs over an odd number of query
     // blocks): the last query and key blocks are partial and positions past the
-    // end do not exist.  A workgroup whose units both lie past the end exits
-    // before the first barrier; a block pair whose second block lies past the end
-    // keeps that unit in the barriers (its rows masked, its decisions unused)
-    // and writes nothing for it.
+    // end do not exist.  An item whose units both lie past the end is done at
+    // once (the workgroup takes its next item); a block pair whose second block
+    // lies past the end keeps that unit in the barriers (its rows masked, its
+    // decisions unused) and writes nothing for it.
     const int n_seq = (RAGGED && p.seq_lens) ? min(max(p.seq_lens[b], 0), p.N) : p.N;
     const int mkv_seq = RAGGED ? (n_seq + BN - 1) / BN : p.Mkv;
     if (RAGGED && i_u[0] * BM >= n_seq) continue;  // i_u[0] <= i_u[1]
