@@ -8,21 +8,21 @@
 namespace bsfa {
 
 // Work counters of the persistent pipelined launches: a ring of slots of 8
-// counters (one per XCD queue) that the library holds in device memory, a copy
-// per device.  Each launch takes the next slot and zeroes it on its own stream
+// 64-bit counters (one per XCD queue) that the library holds in device
+// memory, a copy per device.  Each launch takes the next slot and zeroes it on its own stream
 // before the kernel; a slot comes round again after kWorkSlots launches, so at
 // most that many launches may be in flight at once on one device.
 constexpr int kWorkSlots = 1024;
 constexpr int kMaxDevices = 64;
-static __device__ __align__(256) int work_ring[kWorkSlots][8];
+static __device__ __align__(256) unsigned long long work_ring[kWorkSlots][8];
 
-__global__ void zero_work_slot(int* w) {
+__global__ void zero_work_slot(unsigned long long* w) {
   if (threadIdx.x < 8) w[threadIdx.x] = 0;
 }
 
-int* pipe_work_slot(hipStream_t stream, int* n_cu) {
+unsigned long long* pipe_work_slot(hipStream_t stream, int* n_cu) {
   static std::mutex mu;
-  static int* ring[kMaxDevices];  // the ring's device address on each device
+  static unsigned long long* ring[kMaxDevices];  // the ring's device address on each device
   static int cus[kMaxDevices];
   static std::atomic<unsigned> next{0};
   int dev = -1;
@@ -35,11 +35,11 @@ int* pipe_work_slot(hipStream_t stream, int* n_cu) {
       if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(work_ring)) != hipSuccess || !ptr) return nullptr;
       if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) return nullptr;
       cus[dev] = c;
-      ring[dev] = static_cast<int*>(ptr);
+      ring[dev] = static_cast<unsigned long long*>(ptr);
     }
     *n_cu = cus[dev];
   }
-  int* slot = ring[dev] + 8 * (next.fetch_add(1, std::memory_order_relaxed) % kWorkSlots);
+  unsigned long long* slot = ring[dev] + 8 * (next.fetch_add(1, std::memory_order_relaxed) % kWorkSlots);
   hipLaunchKernelGGL(zero_work_slot, dim3(1), dim3(64), 0, stream, slot);
   if (hipGetLastError() != hipSuccess) return nullptr;
   return slot;

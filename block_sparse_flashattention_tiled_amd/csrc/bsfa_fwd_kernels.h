@@ -288,17 +288,23 @@ __device__ __forceinline__ int xcd_id() { return __builtin_amdgcn_s_getreg((3 <<
 
 // Next work item of a persistent launch over n items.  Queue x holds the
 // items L < n with L % 8 == x in increasing order - the share of the static
-// grid that would run on XCD x, heaviest first - and work[x] counts the items
-// taken from it.  A workgroup drains its own XCD's queue, then takes from the
-// others in turn.  Returns -1 once every queue is empty; counters only grow,
-// so an empty queue stays empty.
-__device__ __forceinline__ int next_item(int* work, int n, int xcd) {
+// grid that would run on XCD x, heaviest first.  A workgroup takes from the
+// front of its own XCD's queue and, once that is empty, from the back of the
+// others in turn, where their lightest items are, so that what moves between
+// XCDs at the end is short.  work[x] packs the items taken from queue x's
+// front (high 32 bits) and back (low 32 bits); one 64-bit atomic add both
+// claims a position and reads how many were claimed before it, so a claim is
+// valid exactly when the claims before it (from either end) leave an item,
+// and the valid claims cover the queue once.  Returns -1 once every queue is
+// empty; counts only grow, so an empty queue stays empty.
+__device__ __forceinline__ int next_item(unsigned long long* work, int n, int xcd) {
   for (int t = 0; t < 8; ++t) {
     const int x = (xcd + t) & 7;
     const int nq = (n - x + 7) >> 3;
     if (nq <= 0) continue;
-    const int idx = atomicAdd(work + x, 1);
-    if (idx < nq) return idx * 8 + x;
+    const unsigned long long old = atomicAdd(work + x, t == 0 ? (1ull << 32) : 1ull);
+    const int front = (int)(old >> 32), back = (int)(old & 0xffffffffu);
+    if (front + back < nq) return (t == 0 ? front : nq - 1 - back) * 8 + x;
   }
   return -1;
 }

@@ -28,7 +28,7 @@ struct FwdParams {
   int gate;          // 0: threshold gate (s_max < tau); 1: gap gate (s_max < running max - tau)
   int pair_h0;       // paired launches: first query head, inside its KV group, that the launch covers
   int pair_hn;       // paired launches: query heads per KV group that the launch covers
-  int* work;         // pipelined (persistent) launches: 8 work-queue counters, zeroed before the launch
+  unsigned long long* work;  // pipelined (persistent) launches: 8 work-queue counters, zeroed before the launch
   int n_items;       // pipelined (persistent) launches: work items (the static grid's workgroups)
 };
 
@@ -47,7 +47,7 @@ int launch_fwd_64x64(const FwdParams& p, int head_dim, int causal, int mode, hip
 // work-queue counters in the library's ring for the current device, enqueued
 // to be zeroed on `stream`, and the device's compute-unit count in *n_cu; null
 // if the ring's device address or the unit count cannot be had.
-int* pipe_work_slot(hipStream_t stream, int* n_cu);
+unsigned long long* pipe_work_slot(hipStream_t stream, int* n_cu);
 
 // Enqueue the fixed-k calibration over tile maxima [S, H, Mq, Mkv] ->
 // thresholds [H, Mq] for B_M x B_N tiles (bm = bn = 1 for square tiles of any

@@ -17,7 +17,7 @@
  *    torch tensors).  No call allocates device memory, and none keeps a
  *    reference after it returns.
  *  - The library's one piece of state is a ring of 1,024 slots of eight
- *    work-queue counters per device (32 KB of module data, loaded with the
+ *    64-bit work-queue counters per device (64 KB of module data, loaded with the
  *    library).  Each launch of the pipelined kernel (128 x 128 tiles at
  *    d = 128; one or two per call) takes the next slot and zeroes it on the
  *    call's stream before the kernel, which then hands out its work items
