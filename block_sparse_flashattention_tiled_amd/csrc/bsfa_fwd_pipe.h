@@ -57,6 +57,12 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   __shared__ int item_sh[2];            // the work item of this and of the next iteration
 
   const int xcd = xcd_id();
+  // This item's Q rows (MFMA B fragments), and whether the previous item's
+  // last step already fetched this item's index (pf_idx) and requested its Q
+  // rows and first two K tiles (pf_loads): the next item's prologue runs under
+  // the last step of the current one.
+  bf16x8 qf[C::KC];
+  int pf_idx = 0, pf_loads = 0;
 
   // Persistent: one workgroup per compute unit takes work items - the
   // workgroups of the static grid - from its XCD's queue until it is empty,
@@ -79,50 +85,77 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int wu = w % P2::NWU;  // wave inside the unit
     const int l32 = lane & 31;
     const int hh = lane >> 5;
-    if (tid == 0) item_sh[iter & 1] = next_item(p.work, n_it, xcd_it);
+    if (!pf_idx) {
+      if (tid == 0) item_sh[iter & 1] = next_item(p.work, n_it, xcd_it);
+    }
+    if (pf_loads) wait_vmem();  // this wave's prefetched Q rows and K_0, K_1
     // also orders the previous item's last LDS reads (and its last loads into
-    // LDS, waited before its last barrier) before this item's loads
+    // LDS, waited before its last barrier) before this item's loads; with the
+    // prologue prefetched, publishes K_0 and K_1
     lds_barrier_keep_dma();
     int L = __builtin_amdgcn_readfirstlane(item_sh[iter & 1]);  // uniform: the loop exit is too
     if (L < 0) break;
+    const bool prefetched = pf_loads;
+    pf_idx = pf_loads = 0;
 
     // ---- work item (a1): item -> (b, KV group, two units); the same mapping as
     // bsfa_fwd_pair_kernel's workgroups -----------------------------------------
-    const int per_group = HEADPAIR ? p.pair_hn / 2 : p.pair_hn;
-    const int n_pairs = (p.M + 1) / 2;
-    int lp = 0;
-    if (HEADPAIR) {
-      if (p.remap) {
-        const int x = L & 7;
-        const int pp = L >> 3;
-        L = ((pp / per_group) * 8 + x) * per_group + (pp % per_group);
+    struct Item {
+      int b, g, hq0, hq1, i0, i1;  // batch, KV group, the two units' query heads and blocks
+    };
+    auto decode = [&](int Li) __attribute__((always_inline)) {
+      const int per_group = HEADPAIR ? p.pair_hn / 2 : p.pair_hn;
+      const int n_pairs = (p.M + 1) / 2;
+      int lp = 0;
+      if (HEADPAIR) {
+        if (p.remap) {
+          const int x = Li & 7;
+          const int pp = Li >> 3;
+          Li = ((pp / per_group) * 8 + x) * per_group + (pp % per_group);
+        }
+      } else if (p.remap) {
+        const int x = Li & 7;
+        const int r = Li >> 3;
+        lp = r % n_pairs;
+        Li = (r / n_pairs) * 8 + x;
+      } else {
+        lp = Li / (p.B * p.Hkv * per_group);
       }
-    } else if (p.remap) {
-      const int x = L & 7;
-      const int r = L >> 3;
-      lp = r % n_pairs;
-      L = (r / n_pairs) * 8 + x;
-    } else {
-      lp = L / (p.B * p.Hkv * per_group);
-    }
-    const int hin = L % per_group;
-    L /= per_group;
-    const int g = L % p.Hkv;
-    L /= p.Hkv;
-    const int b = L % p.B;
-    L /= p.B;
-    int hq_u[2], i_u[2];
-    if (HEADPAIR) {
-      const int i = CAUSAL ? (p.M - 1 - L) : L;  // causal: heaviest query blocks first
-      hq_u[0] = g * p.G + p.pair_h0 + 2 * hin;
-      hq_u[1] = hq_u[0] + 1;
-      i_u[0] = i_u[1] = i;
-    } else {
-      const int ip = CAUSAL ? (n_pairs - 1 - lp) : lp;  // causal: heaviest block pairs first
-      hq_u[0] = hq_u[1] = g * p.G + p.pair_h0 + hin;
-      i_u[0] = 2 * ip;
-      i_u[1] = 2 * ip + 1;
-    }
+      Item it;
+      const int hin = Li % per_group;
+      Li /= per_group;
+      it.g = Li % p.Hkv;
+      Li /= p.Hkv;
+      it.b = Li % p.B;
+      Li /= p.B;
+      if (HEADPAIR) {
+        const int ib = CAUSAL ? (p.M - 1 - Li) : Li;  // causal: heaviest query blocks first
+        it.hq0 = it.g * p.G + p.pair_h0 + 2 * hin;
+        it.hq1 = it.hq0 + 1;
+        it.i0 = it.i1 = ib;
+      } else {
+        const int ip = CAUSAL ? (n_pairs - 1 - lp) : lp;  // causal: heaviest block pairs first
+        it.hq0 = it.hq1 = it.g * p.G + p.pair_h0 + hin;
+        it.i0 = 2 * ip;
+        it.i1 = 2 * ip + 1;
+      }
+      return it;
+    };
+    // an item's sequence length, key blocks and last step (one key tile per
+    // step): the causal diagonal of a head pair, the later diagonal of a causal
+    // block pair (the second unit's, or the first's when the second lies past
+    // the end), the last key tile otherwise
+    auto seq_of = [&](const Item& it) __attribute__((always_inline)) {
+      return (RAGGED && p.seq_lens) ? min(max(p.seq_lens[it.b], 0), p.N) : p.N;
+    };
+    auto last_step = [&](const Item& it, int nseq) __attribute__((always_inline)) {
+      const int mkv = RAGGED ? (nseq + BN - 1) / BN : p.Mkv;
+      return CAUSAL ? (HEADPAIR ? it.i0 : min(it.i1, mkv - 1)) : mkv - 1;
+    };
+    const Item cur = decode(L);
+    const int b = cur.b, g = cur.g;
+    const int hq_u[2] = {cur.hq0, cur.hq1};
+    const int i_u[2] = {cur.i0, cur.i1};
     const int hq = hq_u[u];
     const int i = i_u[u];
     // Tails (RAGGED: a length that is not a multiple of 128, per-sequence
@@ -132,7 +165,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     // once (the workgroup takes its next item); a block pair whose second block
     // lies past the end keeps that unit in the barriers (its rows masked, its
     // decisions unused) and writes nothing for it.
-    const int n_seq = (RAGGED && p.seq_lens) ? min(max(p.seq_lens[b], 0), p.N) : p.N;
+    const int n_seq = seq_of(cur);
     const int mkv_seq = RAGGED ? (n_seq + BN - 1) / BN : p.Mkv;
     if (RAGGED && i_u[0] * BM >= n_seq) continue;  // i_u[0] <= i_u[1]
     const bool live = !RAGGED || i * BM < n_seq;
@@ -152,29 +185,26 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     // ---- (a2) Q: this wave's 32 rows stay in registers as MFMA B fragments ------
     // (a row past the end reads the last row; its scores are masked)
-    bf16x8 qf[C::KC];
-    {
-      const int qr = RAGGED ? min(qrow, n_seq - 1) : qrow;
-      const bf16x8* qsrc = reinterpret_cast<const bf16x8*>(p.q) + (q_head + qr) * (D / 8) + hh;
-  #pragma unroll
+    auto load_q = [&](int b_, int hq_, int i_, int nseq) __attribute__((always_inline)) {
+      const int qr = RAGGED ? min(i_ * BM + qloc, nseq - 1) : i_ * BM + qloc;
+      const bf16x8* qsrc = reinterpret_cast<const bf16x8*>(p.q) + ((size_t)(b_ * p.Hq + hq_) * p.N + qr) * (D / 8) + hh;
+#pragma unroll
       for (int c = 0; c < C::KC; ++c) qf[c] = qsrc[2 * c];
-    }
+    };
+    if (!prefetched) load_q(b, hq, i, n_seq);
     const u32x4* kg = reinterpret_cast<const u32x4*>(p.k) + kv_head * C::CPR;
     const u32x4* vg = reinterpret_cast<const u32x4*>(p.v) + kv_head * C::CPR;
 
     float tau_u[2];
-  #pragma unroll
+    #pragma unroll
     for (int uu = 0; uu < 2; ++uu) tau_u[uu] = p.thresholds[hq_u[uu] * p.T_len + min(i_u[uu], p.T_len - 1)];
     const float c2 = p.scale_log2;
     // square tiles: the diagonal of query block i is key block i
-    // last step (one key tile per step): the causal diagonal of a head pair,
-    // the later diagonal of a causal block pair (the second unit's, or the
-    // first's when the second lies past the end), the last key tile otherwise
-    const int send = CAUSAL ? (HEADPAIR ? i : min(i_u[1], mkv_seq - 1)) : mkv_seq - 1;
+    const int send = last_step(cur, n_seq);
     const size_t diag_row = ((size_t)(b * p.Hq + hq) * p.M + i) * p.Mkv;
 
     f32x16 o[C::DB];
-  #pragma unroll
+    #pragma unroll
     for (int db = 0; db < C::DB; ++db) o[db] = f32x16{};
     float m_run = -INFINITY;
     float l_run = 0.f;
@@ -197,7 +227,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     int v_lane = (lane >> 4) * 256 + (((lane & 15) ^ ((lane >> 4) << 2)) << 4);
     asm volatile("" : "+v"(k_lane), "+v"(v_lane));
     auto dma_tile = [&](char* dst, const u32x4* head, int row0, bool is_k) __attribute__((always_inline)) {
-  #pragma unroll
+      #pragma unroll
       for (int n = 0; n < DMA; ++n) {
         const int chunk0 = (w * DMA + n) * 64;
         const int voff = is_k ? (k_lane ^ (n << 6)) : v_lane;
@@ -207,9 +237,10 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     // The tile that crosses the end of the sequence: lane offsets formed per
     // lane, rows past the end reading the last row (every load stays inside
     // the head); its scores past the end are masked.
-    auto dma_tile_tail = [&](char* dst, const u32x4* head, int row0, bool is_k) __attribute__((always_inline)) {
-      const int last = n_seq - 1 - row0;
-  #pragma unroll
+    auto dma_tile_tail = [&](char* dst, const u32x4* head, int row0, bool is_k, int nseq)
+                             __attribute__((always_inline)) {
+      const int last = nseq - 1 - row0;
+      #pragma unroll
       for (int n = 0; n < DMA; ++n) {
         const int chunk0 = (w * DMA + n) * 64;
         const int row = 4 * (w * DMA + n) + (lane >> 4);
@@ -218,26 +249,50 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
                           row0 * (C::CPR * 16));
       }
     };
-    auto dma_key_tile = [&](char* dst, const u32x4* head, int t, bool is_k) __attribute__((always_inline)) {
-      if (RAGGED && (t + 1) * BN > n_seq) dma_tile_tail(dst, head, t * BN, is_k);
+    auto dma_key_tile_n = [&](char* dst, const u32x4* head, int t, bool is_k, int nseq) __attribute__((always_inline)) {
+      if (RAGGED && (t + 1) * BN > nseq) dma_tile_tail(dst, head, t * BN, is_k, nseq);
       else dma_tile(dst, head, t * BN, is_k);
+    };
+    auto dma_key_tile = [&](char* dst, const u32x4* head, int t, bool is_k) __attribute__((always_inline)) {
+      dma_key_tile_n(dst, head, t, is_k, n_seq);
     };
     // Tile js (K and V alike) lives in buffer (js + par) & 1, so that the last
     // step reads buffer 0 and every buffer choice is known at compile time.
     const int par = send & 1;
-    if (par) dma_key_tile(k_lds1, kg, 0, true);
-    else dma_key_tile(k_lds0, kg, 0, true);
-    wait_vmem();
-    lds_barrier_keep_dma();  // K_0 visible
-    if (send >= 1) {         // K_1, published by the barrier of step 0
-      if (par) dma_key_tile(k_lds0, kg, 1, true);
-      else dma_key_tile(k_lds1, kg, 1, true);
+    if (!prefetched) {
+      if (par) dma_key_tile(k_lds1, kg, 0, true);
+      else dma_key_tile(k_lds0, kg, 0, true);
+      wait_vmem();
+      lds_barrier_keep_dma();  // K_0 visible
+      if (send >= 1) {         // K_1, published by the barrier of step 0
+        if (par) dma_key_tile(k_lds0, kg, 1, true);
+        else dma_key_tile(k_lds1, kg, 1, true);
+      }
     }
+    // The next item's prologue, from the last step once its K tile is read:
+    // its index (fetched before the step's barrier), its Q rows into qf (dead
+    // after this item's last QK^T) and its K_0 and K_1 into the two K tiles
+    // (both free after the last step's barrier).  An item past the end loads
+    // nothing.
+    auto prefetch_next = [&]() __attribute__((always_inline)) {
+      const int Ln = __builtin_amdgcn_readfirstlane(item_sh[(iter + 1) & 1]);
+      pf_idx = 1;
+      if (Ln < 0) return;
+      const Item nx = decode(Ln);
+      const int nseq = seq_of(nx);
+      if (RAGGED && nx.i0 * BM >= nseq) return;
+      load_q(nx.b, u ? nx.hq1 : nx.hq0, u ? nx.i1 : nx.i0, nseq);
+      const int nsend = last_step(nx, nseq);
+      const u32x4* kgn = reinterpret_cast<const u32x4*>(p.k) + (size_t)(nx.b * p.Hkv + nx.g) * p.N * C::CPR;
+      dma_key_tile_n((nsend & 1) ? k_lds1 : k_lds0, kgn, 0, true, nseq);
+      if (nsend >= 1) dma_key_tile_n((nsend & 1) ? k_lds0 : k_lds1, kgn, 1, true, nseq);
+      pf_loads = 1;
+    };
 
     // P~V against the V tile vt: the A fragments (V^T, 32 d x 16 keys) of
     // 16-key chunk kc by transposing LDS reads, then its four MFMAs.
     auto v_frags = [&](const char* vt, int kc, bf16x8 (&a)[C::DB]) __attribute__((always_inline)) {
-  #pragma unroll
+      #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
         const char* base = vt + kc * 16 * (2 * D) + (vb ^ (db << 6));
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
@@ -246,14 +301,14 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
     };
     auto pv_mma = [&](int kc, const bf16x8 (&a)[C::DB]) __attribute__((always_inline)) {
-  #pragma unroll
+      #pragma unroll
       for (int db = 0; db < C::DB; ++db)
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[db], pprev[kc], o[db], 0, 0, 0);
     };
     auto pv_all = [&](const char* vt) __attribute__((always_inline)) {
       bf16x8 a[C::DB];
       v_frags(vt, 0, a);
-  #pragma unroll
+      #pragma unroll
       for (int kc = 0; kc < C::PC; ++kc) {
         pv_mma(kc, a);
         if (kc + 1 < C::PC) v_frags(vt, kc + 1, a);
@@ -261,13 +316,20 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
     };
 
-    auto step = [&](const int js, auto DIAGC, auto KBUF, auto DIAG0C) __attribute__((always_inline)) {
+    auto step = [&](const int js, auto DIAGC, auto KBUF, auto DIAG0C, auto LASTC) __attribute__((always_inline)) {
       constexpr bool DIAG_TILE = decltype(DIAGC)::value;
+      constexpr bool LAST = decltype(LASTC)::value;
       constexpr int kb_cur = decltype(KBUF)::value;
       char* const k_cur = kb_cur ? k_lds1 : k_lds0;       // K_js
       char* const v_cur = kb_cur ? v_lds1 : v_lds0;       // V_js (loaded in this step)
       const char* const v_prev = kb_cur ? v_lds0 : v_lds1;  // V_{js-1} (published by this step's barrier)
       // ---- phase A: (a4) S^T = K Q^T ----------------------------------------
+      // (last step: the next item's index is claimed first, its latency under
+      // the MFMAs, and published by the step's barrier)
+      int nxt = -1;
+      if constexpr (LAST) {
+        if (tid == 0) nxt = next_item(p.work, n_it, xcd_it);
+      }
       f32x16 s[C::KB];
       qk_tile_swz<D, BM, BN>(s, k_cur, l32, hh, qf);
       if constexpr (CAUSAL && DIAG_TILE) mask_causal(s, qloc, hh, i * BM - js * BN);
@@ -282,9 +344,9 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
       // ---- (a5) row maxima and this wave's vote or maximum --------------------
       float rm0 = -INFINITY, rm1 = -INFINITY;
-  #pragma unroll
+      #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
-  #pragma unroll
+        #pragma unroll
         for (int r = 0; r < 16; r += 2) {
           rm0 = vmax(rm0, s[kb][r]);
           rm1 = vmax(rm1, s[kb][r + 1]);
@@ -302,16 +364,20 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
         wm = wave_max_sym(rm);
       }
       if (lane == 0) red[kb_cur][u][wu] = wm;
+      if constexpr (LAST) {
+        if (tid == 0) item_sh[(iter + 1) & 1] = nxt;
+      }
       wait_vmem();             // this wave's loads of K_{js+1} and V_{js-1} have landed
       lds_barrier_keep_dma();  // votes of S_js, K_{js+1} and V_{js-1} complete; K_js and V_{js-2} free
       // ---- phase B ------------------------------------------------------------
       if (!(CAUSAL && DIAG_TILE) && js + 2 <= send) dma_key_tile(k_cur, kg, js + 2, true);
+      if constexpr (LAST) prefetch_next();
       int skip_of[2];
       bool exists_u[2];
-  #pragma unroll
+      #pragma unroll
       for (int uu = 0; uu < 2; ++uu) {
         float tm = red[kb_cur][uu][0];
-  #pragma unroll
+        #pragma unroll
         for (int ww = 1; ww < P2::NWU; ++ww) tm = vmax(tm, red[kb_cur][uu][ww]);
         const float tms = tm * p.scale;
         const bool on_diag = js == i_u[uu];
@@ -353,7 +419,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       // P~_js replaces P~_{js-1}, whose MFMAs are issued first
       auto softmax_chunk = [&](int kc) __attribute__((always_inline)) {
         const int kb = kc / 2, hf = kc % 2;
-  #pragma unroll
+        #pragma unroll
         for (int r = 0; r < 8; r += 2) {
           f32x2 pr;
           pr[0] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hf + r], c2, -m_run));
@@ -368,12 +434,12 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       };
       if (kept_prev) pv_all(v_prev);
       if (kmask) {
-  #pragma unroll
+        #pragma unroll
         for (int kc = 0; kc < C::PC; ++kc) softmax_chunk(kc);
       }
       if (rescale) {
         // after P~V_{js-1}, which is still relative to the old reference
-  #pragma unroll
+        #pragma unroll
         for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
       }
       if (kmask) {
@@ -390,13 +456,14 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     const bool peel0 = CAUSAL && !HEADPAIR && send == i_u[0] + 1;
     const int lend = peel0 ? send - 1 : send;  // steps [0, lend) in the loop
     for (int js = -par; js < lend; js += 2) {
-      if (js >= 0) step(js, std::false_type{}, KB0{}, std::false_type{});
-      if (!(CAUSAL && !HEADPAIR) || js + 1 < lend) step(js + 1, std::false_type{}, KB1{}, std::false_type{});
+      if (js >= 0) step(js, std::false_type{}, KB0{}, std::false_type{}, std::false_type{});
+      if (!(CAUSAL && !HEADPAIR) || js + 1 < lend)
+        step(js + 1, std::false_type{}, KB1{}, std::false_type{}, std::false_type{});
     }
     if constexpr (CAUSAL && !HEADPAIR) {
-      if (peel0) step(send - 1, std::false_type{}, KB1{}, std::true_type{});
+      if (peel0) step(send - 1, std::false_type{}, KB1{}, std::true_type{}, std::false_type{});
     }
-    const int v_last = step(send, std::integral_constant<bool, CAUSAL>{}, KB0{}, std::false_type{});
+    const int v_last = step(send, std::integral_constant<bool, CAUSAL>{}, KB0{}, std::false_type{}, std::true_type{});
     // ---- drain: P~V of the last step (V_send in buffer 0) --------------------------
     if (v_last) {
       wait_vmem();
