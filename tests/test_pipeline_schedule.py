@@ -24,6 +24,11 @@ P~V.  Causal attention: the last step is the diagonal, kept by both units, and
 requests no K.  Every (last step, keep pattern) combination up to 9 steps is
 checked, for head pairs (one diagonal) and block pairs (the second unit's
 diagonal one step later, bidirectional and causal).
+
+The kernel is persistent: in phase B of an item's last step it requests the
+next item's K_0 and K_1 into the two K buffers (by that item's own parity),
+and one more barrier starts the next item, whose step 0 reads K_0 and step 1
+K_1.  With ``next_send`` the model appends those loads and reads.
 """
 
 import itertools
@@ -31,10 +36,11 @@ import itertools
 import pytest
 
 
-def schedule(send, keep, causal):
+def schedule(send, keep, causal, next_send=None):
     """Events (epoch, kind, buffer, tile) of one workgroup.
 
-    keep[u][j]: unit u keeps tile j (diagonal tiles included)."""
+    keep[u][j]: unit u keeps tile j (diagonal tiles included); next_send: the
+    last step of the next item, whose first two K tiles are prefetched."""
     par = send & 1
     kbuf = lambda t: ("K", (t + par) & 1)
     vbuf = lambda t: ("V", (t + par) & 1)
@@ -58,10 +64,24 @@ def schedule(send, keep, causal):
             if kept_prev[u]:
                 ev.append((b, "read", vbuf(j - 1), j - 1))
         kept_prev = [keep[0][j], keep[1][j]]
+    end = send + 2                                   # epoch of the last step's phase B
     if vmask:                                        # drain
+        end += 1
         for u in (0, 1):
             if kept_prev[u]:
                 ev.append((send + 3, "read", vbuf(send), send))
+    if next_send is not None:
+        npar = next_send & 1
+        nk = lambda t: ("K", (t + npar) & 1)
+        ev.append((send + 2, "load", nk(0), ("next", 0)))
+        if next_send >= 1:
+            ev.append((send + 2, "load", nk(1), ("next", 1)))
+        start = end + 1                              # after the item barrier
+        ev.append((start, "read", nk(0), ("next", 0)))   # next item's step 0, phase A
+        if next_send >= 1:
+            ev.append((start + 1, "read", nk(1), ("next", 1)))  # its step 1 (after step 0's barrier)
+            if next_send >= 2:
+                ev.append((start + 1, "load", nk(2), ("next", 2)))  # K_2 requested in step 0's phase B
     return ev
 
 
@@ -157,3 +177,27 @@ def test_model_detects_a_missing_barrier_between_k_load_and_use():
         return ev
     with pytest.raises(AssertionError):
         check(bad(4, [[True] * 5, [True] * 5]))
+
+
+@pytest.mark.parametrize("send", range(0, 7))
+@pytest.mark.parametrize("next_send", range(0, 4))
+def test_next_item_prefetch_has_no_race(send, next_send):
+    # the next item's K_0 and K_1, requested in the last step's phase B, meet
+    # no read of their buffers and are what the next item's first steps read
+    n = send + 1
+    for causal in (True, False):
+        for k in _patterns(n):
+            keep = [list(k), list(k)]
+            if causal:
+                keep[0][send] = keep[1][send] = True
+            check(schedule(send, keep, causal, next_send))
+
+
+def test_model_detects_a_prefetch_before_the_last_read():
+    # requesting the next item's K tiles in phase A of the last step would
+    # overwrite the tile that step is reading
+    ev = schedule(3, [[True] * 4, [True] * 4], True, next_send=2)
+    ev = [(e[0] - 1, e[1], e[2], e[3]) if e[1] == "load" and isinstance(e[3], tuple) and e[3][1] < 2 else e
+          for e in ev]
+    with pytest.raises(AssertionError):
+        check(ev)
