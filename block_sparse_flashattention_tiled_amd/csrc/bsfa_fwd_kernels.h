@@ -327,29 +327,49 @@ __device__ __forceinline__ void lds_barrier_keep_dma() { asm volatile("s_waitcnt
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // S^T = K Q^T with this wave's Q fragments in registers and K from a dense,
-// swizzled tile.
+// swizzled tile.  The MFMAs go in pairs (chunk c, key blocks 2h and 2h + 1),
+// each pair's two K fragments requested two pairs ahead of their use, so that
+// the LDS latency runs under four MFMAs instead of stalling the next one.
 template <int D, int BM, int BN, int NKB, int NKC>
 __device__ __forceinline__ void qk_tile_swz(f32x16 (&s)[NKB], const char* ks, int l32, int hh,
                                             const bf16x8 (&qf)[NKC]) {
   using C = Cfg<D, BM, BN>;
   static_assert(NKB == C::KB && NKC == C::KC, "fragment sizes");
+  static_assert(C::KB % 2 == 0 && C::KC * C::KB >= 4, "pairs of key blocks, at least two pairs");
   // Chunk 2c + hh of row l32 (rows kb*32 + l32 share the swizzle x) sits at
   // byte l32 2D + ((2c + hh) ^ x) 16 = bx ^ 32c: the row, the bit of hh and
   // the bits of c occupy disjoint address bits.  bx is made opaque so that
-  // the eight addresses are formed at each use rather than held in registers.
+  // the addresses are formed at each use rather than held in registers.
   const int x = k_swz<D>(l32);
   int bx = l32 * (2 * D) + ((hh ^ (x & 1)) << 4) + ((x & ~1) << 4);
   asm volatile("" : "+v"(bx));
 #pragma unroll
   for (int kb = 0; kb < C::KB; ++kb) s[kb] = f32x16{};
+  constexpr int NP = C::KC * C::KB / 2;  // MFMA pairs
+  auto frag = [&](int q, int e) __attribute__((always_inline)) {
+    const int c = q / (C::KB / 2), h = q % (C::KB / 2);
+    return *reinterpret_cast<const bf16x8*>(ks + (bx ^ (c << 5)) + (2 * h + e) * 32 * 2 * D);
+  };
+  bf16x8 a0 = frag(0, 0), a1 = frag(0, 1), b0 = frag(1, 0), b1 = frag(1, 1);
 #pragma unroll
-  for (int c = 0; c < C::KC; ++c) {
-    const char* kc = ks + (bx ^ (c << 5));
-    bf16x8 a[C::KB];
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) a[kb] = *reinterpret_cast<const bf16x8*>(kc + kb * 32 * 2 * D);
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], qf[c], s[kb], 0, 0, 0);
+  for (int q = 0; q < NP; ++q) {
+    bf16x8 n0, n1;
+    if (q + 2 < NP) {
+      n0 = frag(q + 2, 0);
+      n1 = frag(q + 2, 1);
+    }
+    const int c = q / (C::KB / 2), h = q % (C::KB / 2);
+    s[2 * h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[c], s[2 * h], 0, 0, 0);
+    s[2 * h + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[c], s[2 * h + 1], 0, 0, 0);
+    a0 = b0;
+    a1 = b1;
+    if (q + 2 < NP) {
+      b0 = n0;
+      b1 = n1;
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the reads two pairs ahead first
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);    // then this pair's MFMAs
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 

@@ -188,7 +188,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     auto load_q = [&](int b_, int hq_, int i_, int nseq) __attribute__((always_inline)) {
       const int qr = RAGGED ? min(i_ * BM + qloc, nseq - 1) : i_ * BM + qloc;
       const bf16x8* qsrc = reinterpret_cast<const bf16x8*>(p.q) + ((size_t)(b_ * p.Hq + hq_) * p.N + qr) * (D / 8) + hh;
-#pragma unroll
+      #pragma unroll
       for (int c = 0; c < C::KC; ++c) qf[c] = qsrc[2 * c];
     };
     if (!prefetched) load_q(b, hq, i, n_seq);
@@ -289,29 +289,32 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       pf_loads = 1;
     };
 
-    // P~V against the V tile vt: the A fragments (V^T, 32 d x 16 keys) of
-    // 16-key chunk kc by transposing LDS reads, then its four MFMAs.
-    auto v_frags = [&](const char* vt, int kc, bf16x8 (&a)[C::DB]) __attribute__((always_inline)) {
-      #pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        const char* base = vt + kc * 16 * (2 * D) + (vb ^ (db << 6));
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * 2 * D));
-        a[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-    };
-    auto pv_mma = [&](int kc, const bf16x8 (&a)[C::DB]) __attribute__((always_inline)) {
-      #pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[db], pprev[kc], o[db], 0, 0, 0);
+    // P~V against the V tile vt.  v_frag: the A fragment (V^T, 32 d x 16
+    // keys) of column block db and 16-key chunk kc, by two transposing LDS
+    // reads.  pv_all: every chunk's four MFMAs, each fragment of chunk kc + 1
+    // requested right after the MFMA that consumed the same registers for chunk
+    // kc, so that it has four MFMAs to land.
+    auto v_frag = [&](const char* vt, int kc, int db) __attribute__((always_inline)) {
+      const char* base = vt + kc * 16 * (2 * D) + (vb ^ (db << 6));
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * 2 * D));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     auto pv_all = [&](const char* vt) __attribute__((always_inline)) {
       bf16x8 a[C::DB];
-      v_frags(vt, 0, a);
+      #pragma unroll
+      for (int db = 0; db < C::DB; ++db) a[db] = v_frag(vt, 0, db);
       #pragma unroll
       for (int kc = 0; kc < C::PC; ++kc) {
-        pv_mma(kc, a);
-        if (kc + 1 < C::PC) v_frags(vt, kc + 1, a);
+        #pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[db], pprev[kc], o[db], 0, 0, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (kc + 1 < C::PC) {
+            a[db] = v_frag(vt, kc + 1, db);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     };
