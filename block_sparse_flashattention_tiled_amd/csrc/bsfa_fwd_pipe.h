@@ -199,6 +199,14 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     #pragma unroll
     for (int uu = 0; uu < 2; ++uu) tau_u[uu] = p.thresholds[hq_u[uu] * p.T_len + min(i_u[uu], p.T_len - 1)];
     const float c2 = p.scale_log2;
+    // Arguments read inside the step loop, held in registers: every barrier is
+    // a compiler memory barrier, after which a read through p would be issued
+    // again (a scalar load and its wait on the critical path of each step).
+    const float scale = p.scale;
+    const int gate = p.gate;
+    const int kv_bytes = p.N * D * 2;  // one head's K or V: the range of its buffer loads
+    uint8_t* const tile_state = p.tile_state;
+    float* const tile_max = p.tile_max;
     // square tiles: the diagonal of query block i is key block i
     const int send = last_step(cur, n_seq);
     const size_t diag_row = ((size_t)(b * p.Hq + hq) * p.M + i) * p.Mkv;
@@ -231,7 +239,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       for (int n = 0; n < DMA; ++n) {
         const int chunk0 = (w * DMA + n) * 64;
         const int voff = is_k ? (k_lane ^ (n << 6)) : v_lane;
-        buffer_load_lds16(head, p.N * D * 2, dst + chunk0 * 16, voff, row0 * (C::CPR * 16) + chunk0 * 16);
+        buffer_load_lds16(head, kv_bytes, dst + chunk0 * 16, voff, row0 * (C::CPR * 16) + chunk0 * 16);
       }
     };
     // The tile that crosses the end of the sequence: lane offsets formed per
@@ -245,7 +253,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int chunk0 = (w * DMA + n) * 64;
         const int row = 4 * (w * DMA + n) + (lane >> 4);
         const int cc = (lane & 15) ^ (is_k ? k_swz<D>(row) : v_swz<D>(row));
-        buffer_load_lds16(head, p.N * D * 2, dst + chunk0 * 16, (min(row, last) * C::CPR + cc) * 16,
+        buffer_load_lds16(head, kv_bytes, dst + chunk0 * 16, (min(row, last) * C::CPR + cc) * 16,
                           row0 * (C::CPR * 16));
       }
     };
@@ -357,11 +365,11 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       float rm = vmax(rm0, rm1);
       rm = max_halves(rm);
       float wm;
-      if (!DIAG_OUT && p.gate == 0) {
+      if (!DIAG_OUT && gate == 0) {
         // threshold gate without tile maxima written: each wave votes +inf if
         // some row's scaled maximum is not below tau (rounding of the positive
         // scale is monotone: the decision the tile maximum gives, NaN included)
-        const bool keep = !(rm * p.scale < (u ? tau_u[1] : tau_u[0]));
+        const bool keep = !(rm * scale < (u ? tau_u[1] : tau_u[0]));
         wm = __builtin_amdgcn_ballot_w64(keep) ? INFINITY : -INFINITY;
       } else {
         wm = wave_max_sym(rm);
@@ -382,14 +390,14 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
         float tm = red[kb_cur][uu][0];
         #pragma unroll
         for (int ww = 1; ww < P2::NWU; ++ww) tm = vmax(tm, red[kb_cur][uu][ww]);
-        const float tms = tm * p.scale;
+        const float tms = tm * scale;
         const bool on_diag = js == i_u[uu];
         // in a causal block pair the first unit has no tile past its diagonal
         exists_u[uu] = !CAUSAL || HEADPAIR || js <= i_u[uu];
-        skip_of[uu] = exists_u[uu] ? gate_skip(p.gate, !on_diag, tms, tau_u[uu], mrun_u[uu]) : 1;
+        skip_of[uu] = exists_u[uu] ? gate_skip(gate, !on_diag, tms, tau_u[uu], mrun_u[uu]) : 1;
         if (DIAG_OUT && exists_u[uu] && uu == u && wu == 0 && lane == 0 && live) {
-          if (p.tile_state) p.tile_state[diag_row + js] = on_diag ? 3 : (skip_of[uu] ? 2 : 1);
-          if (p.tile_max) p.tile_max[diag_row + js] = tms;
+          if (tile_state) tile_state[diag_row + js] = on_diag ? 3 : (skip_of[uu] ? 2 : 1);
+          if (tile_max) tile_max[diag_row + js] = tms;
         }
       }
       const int mine = u ? skip_of[1] : skip_of[0];
